@@ -1,0 +1,179 @@
+/*
+ * pagedattn.h -- C ABI of a gfx950 (MI355X) library for attention over a
+ * paged KV cache.
+ *
+ * The method (devpress.csdn.net page, sections "PagedAttention 是如何工作的"
+ * and "分页式KV缓存"; aidocs.cortexgrid.cn page, intro bullets and FAQ;
+ * betteryeah.com page, sections 2.2 and 2.4): the KV cache of every sequence
+ * is cut into fixed-size blocks of block_size tokens (16 or 32) that may sit
+ * anywhere in one pool; a per-sequence block table maps logical block i to a
+ * physical block; attention follows the table across the scattered blocks.
+ * Sequences that share a prefix (parallel sampling) list the same physical
+ * blocks in their tables; the kernels only read them.
+ *
+ * Conventions for every call:
+ *  - Tensor pointers are DEVICE pointers owned by the caller. The library
+ *    allocates nothing, keeps no pointer after returning, holds no global
+ *    mutable state and is safe to call from several host threads.
+ *  - Work is queued on `stream` and never synchronised; the library never
+ *    reads device memory on the host.
+ *  - Validation is host-side on scalars and pointer nullness only; a failed
+ *    check returns an error before anything is launched. Data preconditions
+ *    (listed per call) are the caller's duty and are not checked on device.
+ *  - Layouts (row-major, contiguous):
+ *      k_cache, v_cache  [num_blocks][num_heads][block_size][head_dim]
+ *      block_tables      int32 [num_seqs][max_blocks_per_seq]
+ *      q, out            [rows][num_heads][head_dim]
+ *    A slot is block * block_size + offset.
+ *  - Supported: head_dim 64 or 128, block_size 16 or 32, num_kv_heads ==
+ *    num_heads, dtype f32/f16/bf16; out_dtype is PA_F32 or equal to dtype.
+ *    Accumulation is fp32; a narrower output is rounded to nearest even from
+ *    the fp32 result.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, inconsistent sizes */
+  PA_ERR_UNSUPPORTED = -2, /* head_dim, block_size, dtype or head layout not built */
+  PA_ERR_WORKSPACE = -3,   /* split-K workspace missing or too small */
+  PA_ERR_HIP = -4          /* a launch failed; hipGetLastError() was cleared */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/* Human-readable name of a status code (static storage). */
+const char* pa_status_string(pa_status status);
+
+/*
+ * reshape_and_cache -- write this step's new tokens into their cache slots.
+ * New tokens get slots in blocks handed out on demand (devpress page,
+ * "实际收益远超预期" and workflow step "分页加载"; betteryeah page, section
+ * 2.2). For every n < num_tokens with slot_mapping[n] >= 0 and every head h:
+ *   k_cache[slot/bs][h][slot%bs][:] = k[n][h][:]   (same for v)
+ * bit for bit. Rows with a negative slot are skipped; every other cache slot
+ * is left untouched.
+ *   k, v          [num_tokens][num_heads][head_dim], dtype
+ *   slot_mapping  int32 [num_tokens]
+ * Preconditions: non-negative slots are distinct and < num_blocks*block_size.
+ * num_tokens == 0 is a no-op. Errors: INVALID_ARG (null pointer, sizes,
+ * num_blocks*block_size > INT32_MAX), UNSUPPORTED, HIP.
+ */
+pa_status pa_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                               const int32_t* slot_mapping, int32_t num_tokens, int32_t num_heads,
+                               int32_t head_dim, int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                               hipStream_t stream);
+
+/*
+ * gather_kv -- materialise each sequence's logical K and V contiguously
+ * through its block table (the translation every attention kernel uses):
+ *   k_out[cu_context_lens[s] + t][h][:] = k_cache[bt[s][t/bs]][h][t%bs][:]
+ * for t < context_lens[s]; same for v. Bit-exact copy, for checking the
+ * table translation and for debugging.
+ *   cu_context_lens  int32 [num_seqs+1], exclusive prefix sum of context_lens
+ *   max_context_len  >= every context_lens[s] (sizes the grid)
+ * Preconditions: table entries below ceil(ctx/bs) are valid block ids.
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP.
+ */
+pa_status pa_gather_kv(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens,
+                       const int32_t* cu_context_lens, int32_t num_seqs, int32_t max_context_len,
+                       int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                       int32_t max_blocks_per_seq, pa_dtype dtype, hipStream_t stream);
+
+/*
+ * Split-K sizing for decode. Contexts are cut into partitions of
+ * pa_decode_partition_tokens() tokens (a whole number of blocks). The
+ * workspace holds fp32 partials (m, l, acc[head_dim]) for every (sequence,
+ * head, partition): pa_decode_workspace_bytes() bytes, or 0 when
+ * max_context_len fits one partition (then no workspace is needed).
+ */
+int32_t pa_decode_partition_tokens(void);
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                 int32_t max_context_len);
+
+/*
+ * paged_attention_decode -- one query per sequence attends to all of its
+ * context_lens[s] cached tokens (the current token included: it is written by
+ * pa_reshape_and_cache first):
+ *   out[s][h] = softmax_t(scale * <q[s][h], K_t>) . V_t,  t < context_lens[s]
+ * with K_t, V_t read through block_tables[s] (scaled dot-product attention is
+ * the reading of "attention" used here; the pages do not write the formula).
+ *   q           [num_seqs][num_heads][head_dim], dtype
+ *   out         [num_seqs][num_heads][head_dim], out_dtype
+ *   workspace   NULL disables split-K (one partition per sequence); otherwise
+ *               at least pa_decode_workspace_bytes(...) bytes, fp32-aligned.
+ * context_lens[s] == 0 gives a zero output row.
+ * Preconditions: context_lens[s] <= max_context_len <= max_blocks_per_seq *
+ * block_size; table entries below ceil(ctx/bs) are valid block ids; entries
+ * past them, and cache slots past a context, are never read.
+ * Launches K2 (partitions) and, when any partial exists, K3 (reduction).
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
+ */
+pa_status pa_paged_attention_decode(void* out, pa_dtype out_dtype, const void* q, const void* k_cache,
+                                    const void* v_cache, const int32_t* block_tables,
+                                    const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                    int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                                    float scale, pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
+/*
+ * The two stages of pa_paged_attention_decode, for callers that schedule or
+ * time them separately. _partitions takes the same arguments and launches K2
+ * only; _reduce then merges the partials of rows with more than one
+ * partition. Together they equal pa_paged_attention_decode bit for bit.
+ */
+pa_status pa_paged_attention_decode_partitions(void* out, pa_dtype out_dtype, const void* q,
+                                               const void* k_cache, const void* v_cache,
+                                               const int32_t* block_tables, const int32_t* context_lens,
+                                               int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                               int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                               int32_t max_blocks_per_seq, int32_t max_context_len,
+                                               float scale, pa_dtype dtype, void* workspace,
+                                               size_t workspace_bytes, hipStream_t stream);
+pa_status pa_paged_attention_decode_reduce(void* out, pa_dtype out_dtype, const int32_t* context_lens,
+                                           int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                           int32_t max_context_len, pa_dtype dtype, const void* workspace,
+                                           size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * paged_attention_prefill -- causal attention of multi-token query chunks
+ * over the paged cache. Sequence s owns query rows query_start_loc[s] ..
+ * query_start_loc[s+1]-1 (L_s >= 0 of them); its context context_lens[s]
+ * INCLUDES the chunk, whose K/V are already cached, so the chunk is the last
+ * L_s tokens: row query_start_loc[s] + j sits at position ctx - L_s + j and
+ * attends to tokens 0 .. ctx - L_s + j.
+ *   q, out           [total_q][num_heads][head_dim]
+ *   query_start_loc  int32 [num_seqs+1], query_start_loc[0] == 0,
+ *                    query_start_loc[num_seqs] == total_q
+ *   max_q_len        >= every L_s (sizes the grid)
+ * f16/bf16 run on matrix cores (MFMA, fp32 accumulate, P rounded to the
+ * input dtype before the P.V product); f32 runs on the vector path.
+ * Preconditions: non-decreasing query_start_loc, L_s <= context_lens[s] <=
+ * max_context_len <= max_blocks_per_seq * block_size, valid table entries.
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP.
+ */
+pa_status pa_paged_attention_prefill(void* out, pa_dtype out_dtype, const void* q, const void* k_cache,
+                                     const void* v_cache, const int32_t* block_tables,
+                                     const int32_t* context_lens, const int32_t* query_start_loc,
+                                     int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t num_heads,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                     int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                                     float scale, pa_dtype dtype, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

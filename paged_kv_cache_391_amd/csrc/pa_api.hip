@@ -1,0 +1,265 @@
+// C ABI: host-side validation and kernel dispatch. No allocation, no device
+// reads, no global mutable state.
+#include <limits.h>
+#include <math.h>
+
+#include "../../include/pagedattn.h"
+#include "pa_internal.h"
+
+namespace {
+
+using pa::Dt;
+
+bool dtype_ok(pa_dtype d) { return d == PA_F32 || d == PA_F16 || d == PA_BF16; }
+int elt_bytes(pa_dtype d) { return d == PA_F32 ? 4 : 2; }
+bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
+bool block_size_ok(int32_t b) { return b == 16 || b == 32; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+pa_status hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+pa_status check_cache_shape(int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                            pa_dtype dtype) {
+  if (num_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0) return PA_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
+  if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)num_blocks * block_size > INT32_MAX) return PA_ERR_INVALID_ARG;  // slots are int32
+  return PA_OK;
+}
+
+int64_t max_parts_for(int32_t max_context_len) {
+  return max_context_len <= 0 ? 1 : ceil_div(max_context_len, pa::kPartitionTokens);
+}
+
+struct DecodeCall {
+  pa::DecodeArgs args;
+  Dt dt;
+  int D, BS;
+  bool split;
+};
+
+pa_status prepare_decode(DecodeCall& call, void* out, pa_dtype out_dtype, const void* q, const void* k_cache,
+                         const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                         int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                         int32_t max_context_len, float scale, pa_dtype dtype, void* workspace,
+                         size_t workspace_bytes) {
+  pa_status st = check_cache_shape(num_heads, head_dim, block_size, num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0) return PA_ERR_INVALID_ARG;
+  if (num_kv_heads != num_heads) return PA_ERR_UNSUPPORTED;
+  if (out_dtype != PA_F32 && out_dtype != dtype) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (num_seqs > 0 && (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens))
+    return PA_ERR_INVALID_ARG;
+  const int64_t parts = max_parts_for(max_context_len);
+  bool split = parts > 1 && workspace != nullptr;
+  if (split && workspace_bytes < pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len))
+    return PA_ERR_WORKSPACE;
+  if (split && ((uintptr_t)workspace % 16) != 0) return PA_ERR_WORKSPACE;
+  const int64_t grid_parts = split ? parts : 1;
+  if ((int64_t)num_seqs * num_heads * grid_parts > INT32_MAX) return PA_ERR_INVALID_ARG;
+  pa::DecodeArgs& a = call.args;
+  a.out = out;
+  a.ws = split ? static_cast<float*>(workspace) : nullptr;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start_loc = nullptr;
+  a.num_rows = num_seqs;
+  a.num_seqs = num_seqs;
+  a.H = num_heads;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_parts = (int)grid_parts;
+  // without split-K one partition spans the longest context
+  a.part_tiles = split ? pa::kPartitionTokens / 16 : (int)std::max<int64_t>(1, ceil_div(max_context_len, 16));
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out_f32 = out_dtype == PA_F32 ? 1 : 0;
+  call.dt = static_cast<Dt>(dtype);
+  call.D = head_dim;
+  call.BS = block_size;
+  call.split = split;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(pa_status status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_WORKSPACE: return "split-K workspace missing, misaligned or too small";
+    case PA_ERR_HIP: return "HIP launch failure";
+  }
+  return "unknown status";
+}
+
+pa_status pa_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                               const int32_t* slot_mapping, int32_t num_tokens, int32_t num_heads,
+                               int32_t head_dim, int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                               hipStream_t stream) {
+  pa_status st = check_cache_shape(num_heads, head_dim, block_size, num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PA_ERR_INVALID_ARG;
+  return hip_status(pa::launch_reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, num_tokens, num_heads,
+                                                 head_dim, block_size, elt_bytes(dtype), stream));
+}
+
+pa_status pa_gather_kv(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens,
+                       const int32_t* cu_context_lens, int32_t num_seqs, int32_t max_context_len,
+                       int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                       int32_t max_blocks_per_seq, pa_dtype dtype, hipStream_t stream) {
+  pa_status st = check_cache_shape(num_heads, head_dim, block_size, num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_seqs > 65535 || max_context_len < 0 || max_blocks_per_seq <= 0)
+    return PA_ERR_INVALID_ARG;
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0 || max_context_len == 0) return PA_OK;
+  if (!k_out || !v_out || !k_cache || !v_cache || !block_tables || !context_lens || !cu_context_lens)
+    return PA_ERR_INVALID_ARG;
+  return hip_status(pa::launch_gather_kv(k_out, v_out, k_cache, v_cache, block_tables, context_lens,
+                                         cu_context_lens, num_seqs, max_context_len, num_heads, head_dim,
+                                         block_size, max_blocks_per_seq, elt_bytes(dtype), stream));
+}
+
+int32_t pa_decode_partition_tokens(void) { return pa::kPartitionTokens; }
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                 int32_t max_context_len) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+  const int64_t parts = max_parts_for(max_context_len);
+  if (parts <= 1) return 0;
+  return (size_t)num_seqs * num_heads * parts * (head_dim + 2) * sizeof(float);
+}
+
+pa_status pa_paged_attention_decode_partitions(void* out, pa_dtype out_dtype, const void* q,
+                                               const void* k_cache, const void* v_cache,
+                                               const int32_t* block_tables, const int32_t* context_lens,
+                                               int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                               int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                               int32_t max_blocks_per_seq, int32_t max_context_len,
+                                               float scale, pa_dtype dtype, void* workspace,
+                                               size_t workspace_bytes, hipStream_t stream) {
+  DecodeCall call;
+  pa_status st = prepare_decode(call, out, out_dtype, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                                num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                max_context_len, scale, dtype, workspace, workspace_bytes);
+  if (st != PA_OK || num_seqs == 0) return st;
+  return hip_status(pa::launch_decode_partitions(call.args, call.dt, call.D, call.BS, false, stream));
+}
+
+pa_status pa_paged_attention_decode_reduce(void* out, pa_dtype out_dtype, const int32_t* context_lens,
+                                           int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                           int32_t max_context_len, pa_dtype dtype, const void* workspace,
+                                           size_t workspace_bytes, hipStream_t stream) {
+  if (num_seqs < 0 || num_heads <= 0 || max_context_len < 0) return PA_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype) || !head_dim_ok(head_dim)) return PA_ERR_UNSUPPORTED;
+  if (out_dtype != PA_F32 && out_dtype != dtype) return PA_ERR_UNSUPPORTED;
+  const int64_t parts = max_parts_for(max_context_len);
+  if (num_seqs == 0 || parts <= 1 || workspace == nullptr) return PA_OK;  // nothing was split
+  if (workspace_bytes < pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len))
+    return PA_ERR_WORKSPACE;
+  if (!out || !context_lens) return PA_ERR_INVALID_ARG;
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.ws = static_cast<float*>(const_cast<void*>(workspace));
+  a.context_lens = context_lens;
+  a.num_rows = num_seqs;
+  a.num_seqs = num_seqs;
+  a.H = num_heads;
+  a.max_parts = (int)parts;
+  a.part_tiles = pa::kPartitionTokens / 16;
+  a.out_f32 = out_dtype == PA_F32 ? 1 : 0;
+  return hip_status(pa::launch_decode_reduce(a, static_cast<Dt>(dtype), head_dim, stream));
+}
+
+pa_status pa_paged_attention_decode(void* out, pa_dtype out_dtype, const void* q, const void* k_cache,
+                                    const void* v_cache, const int32_t* block_tables,
+                                    const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                    int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                                    float scale, pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  DecodeCall call;
+  pa_status st = prepare_decode(call, out, out_dtype, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                                num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                max_context_len, scale, dtype, workspace, workspace_bytes);
+  if (st != PA_OK || num_seqs == 0) return st;
+  hipError_t e = pa::launch_decode_partitions(call.args, call.dt, call.D, call.BS, false, stream);
+  if (e == hipSuccess && call.split) e = pa::launch_decode_reduce(call.args, call.dt, call.D, stream);
+  return hip_status(e);
+}
+
+pa_status pa_paged_attention_prefill(void* out, pa_dtype out_dtype, const void* q, const void* k_cache,
+                                     const void* v_cache, const int32_t* block_tables,
+                                     const int32_t* context_lens, const int32_t* query_start_loc,
+                                     int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t num_heads,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                     int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                                     float scale, pa_dtype dtype, hipStream_t stream) {
+  pa_status st = check_cache_shape(num_heads, head_dim, block_size, num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || max_blocks_per_seq <= 0 || max_context_len < 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_kv_heads != num_heads) return PA_ERR_UNSUPPORTED;
+  if (out_dtype != PA_F32 && out_dtype != dtype) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_INVALID_ARG;
+  if (max_q_len > max_context_len || (num_seqs > 0 && total_q > (int64_t)num_seqs * max_q_len))
+    return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0 || total_q == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc)
+    return PA_ERR_INVALID_ARG;
+  const float scale_log2 = scale * 1.4426950408889634f;
+  if (dtype != PA_F32) {
+    pa::PrefillArgs a{};
+    a.out = out;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.query_start_loc = query_start_loc;
+    a.num_seqs = num_seqs;
+    a.total_q = total_q;
+    a.H = num_heads;
+    a.max_blocks = max_blocks_per_seq;
+    a.max_context_len = max_context_len;
+    a.q_tiles = (int)ceil_div(max_q_len, pa::prefill_mfma_q_tile());
+    a.scale_log2 = scale_log2;
+    a.out_f32 = out_dtype == PA_F32 ? 1 : 0;
+    if ((int64_t)a.q_tiles * num_heads * num_seqs > INT32_MAX) return PA_ERR_INVALID_ARG;
+    return hip_status(pa::launch_prefill_mfma(a, static_cast<Dt>(dtype), head_dim, block_size, stream));
+  }
+  // fp32: every query row is a decode over its own causal prefix
+  if ((int64_t)total_q * num_heads > INT32_MAX) return PA_ERR_INVALID_ARG;
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.ws = nullptr;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start_loc = query_start_loc;
+  a.num_rows = total_q;
+  a.num_seqs = num_seqs;
+  a.H = num_heads;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_parts = 1;
+  a.part_tiles = (int)std::max<int64_t>(1, ceil_div(max_context_len, 16));
+  a.scale_log2 = scale_log2;
+  a.out_f32 = 1;
+  return hip_status(pa::launch_decode_partitions(a, Dt::F32, head_dim, block_size, true, stream));
+}
+
+}  // extern "C"

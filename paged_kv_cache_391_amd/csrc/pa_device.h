@@ -1,0 +1,89 @@
+// Device-side helpers shared by every kernel of the library: element types,
+// exact widening, round-to-nearest-even narrowing, the paged address
+// translation and 16-lane row reductions.
+//
+// Target: gfx950 (CDNA4), wave64.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+
+enum class Dt : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+template <Dt DT> struct ElemT;
+template <> struct ElemT<Dt::F32> { using storage = uint32_t; static constexpr int bytes = 4; };
+template <> struct ElemT<Dt::F16> { using storage = uint16_t; static constexpr int bytes = 2; };
+template <> struct ElemT<Dt::BF16> { using storage = uint16_t; static constexpr int bytes = 2; };
+
+// ---- widening (exact) -----------------------------------------------------
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// element `i` (0/1) of a packed 32-bit word holding two 16-bit values, or
+// the word itself for fp32
+template <Dt DT> __device__ __forceinline__ float widen_lo(uint32_t w) {
+  if constexpr (DT == Dt::F32) return __uint_as_float(w);
+  else if constexpr (DT == Dt::F16) return f16_bits_to_f32(w & 0xffffu);
+  else return __uint_as_float(w << 16);
+}
+template <Dt DT> __device__ __forceinline__ float widen_hi(uint32_t w) {
+  if constexpr (DT == Dt::F16) return f16_bits_to_f32(w >> 16);
+  else return __uint_as_float(w & 0xffff0000u);
+}
+
+// ---- narrowing (round to nearest even) -------------------------------------
+
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float x) {
+  // v_cvt_f16_f32 rounds with the default round-to-nearest-even mode
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // keep NaN quiet
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// ---- paged address translation ---------------------------------------------
+// Caches are [num_blocks][H][BS][D]. Logical token t of a sequence lives in
+// physical block table[t / BS] at offset t % BS; one (block, head) tile of
+// BS*D elements is contiguous.
+
+__device__ __forceinline__ int64_t kv_tile_offset(int32_t phys_block, int head, int H, int BS, int D) {
+  return ((int64_t)phys_block * H + head) * (int64_t)BS * D;
+}
+__device__ __forceinline__ int64_t kv_row_offset(int32_t phys_block, int head, int off, int H, int BS, int D) {
+  return kv_tile_offset(phys_block, head, H, BS, D) + (int64_t)off * D;
+}
+
+// ---- reductions over the 16 lanes of a DPP row ------------------------------
+// quad_perm [1,0,3,2] and [2,3,0,1] exchange within quads, row_half_mirror
+// pairs the two quads of each half-row and row_mirror the two half-rows, so
+// after four steps every lane of the row holds the row total.
+
+template <int CTRL> __device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f<0xB1>(x);   // quad_perm(1,0,3,2)
+  x += dpp_f<0x4E>(x);   // quad_perm(2,3,0,1)
+  x += dpp_f<0x141>(x);  // row_half_mirror
+  x += dpp_f<0x140>(x);  // row_mirror
+  return x;
+}
+
+// xor shuffle across the whole wave (through ds_bpermute)
+__device__ __forceinline__ float shfl_xor_f(float x, int m) {
+  int lane = __lane_id();
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ m) << 2, __builtin_bit_cast(int, x)));
+}
+
+}  // namespace pa

@@ -1,0 +1,78 @@
+// Host-side launcher declarations shared between the C-ABI layer and the
+// kernel files. Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_device.h"
+
+// Decode tuning: waves per workgroup and tokens per split-K partition.
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 4
+#endif
+#ifndef PA_PARTITION_TOKENS
+#define PA_PARTITION_TOKENS 512
+#endif
+
+namespace pa {
+
+constexpr int kDecodeWaves = PA_DECODE_WAVES;
+constexpr int kPartitionTokens = PA_PARTITION_TOKENS;
+static_assert(kPartitionTokens % 32 == 0, "partitions must hold whole 16- and 32-token blocks");
+
+struct DecodeArgs {
+  void* out;                        // [rows][H][D], fp32 or the input dtype
+  float* ws;                        // split-K partials (nullptr: single partition)
+  const void* q;                    // [rows][H][D]
+  const void* k_cache;              // [num_blocks][H][BS][D]
+  const void* v_cache;
+  const int32_t* block_tables;      // [num_seqs][max_blocks]
+  const int32_t* context_lens;      // [num_seqs]
+  const int32_t* query_start_loc;   // [num_seqs+1], prefill-row mode only
+  int num_rows;                     // decode: num_seqs; prefill-row mode: total queries
+  int num_seqs;
+  int H;
+  int max_blocks;
+  int max_parts;                    // partitions per row in the grid
+  int part_tiles;                   // 16-token tiles per partition
+  float scale_log2;                 // scale * log2(e)
+  int out_f32;
+};
+
+hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                                    const int32_t* slot_mapping, int T, int H, int D, int BS, int elt_bytes,
+                                    hipStream_t stream);
+hipError_t launch_gather_kv(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens, const int32_t* cu_ctx,
+                            int S, int max_ctx, int H, int D, int BS, int max_blocks, int elt_bytes,
+                            hipStream_t stream);
+
+// partition kernel (K2); prefill_rows selects the per-query-row mode
+hipError_t launch_decode_partitions(const DecodeArgs& a, Dt dt, int D, int BS, bool prefill_rows,
+                                    hipStream_t stream);
+// reduction kernel (K3)
+hipError_t launch_decode_reduce(const DecodeArgs& a, Dt dt, int D, hipStream_t stream);
+
+// MFMA causal prefill (K4), fp16/bf16 only
+struct PrefillArgs {
+  void* out;                        // [total_q][H][D]
+  const void* q;                    // [total_q][H][D]
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start_loc;
+  int num_seqs;
+  int total_q;
+  int H;
+  int max_blocks;
+  int max_context_len;
+  int q_tiles;                      // grid: q tiles per sequence
+  float scale_log2;
+  int out_f32;
+};
+hipError_t launch_prefill_mfma(const PrefillArgs& a, Dt dt, int D, int BS, hipStream_t stream);
+int prefill_mfma_q_tile();
+
+}  // namespace pa

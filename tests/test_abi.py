@@ -1,0 +1,137 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments host-side (before any launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_391_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedattn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(pa.LIB_PATH), reason="libpagedattn.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_calls():
+    names = _declared()
+    for n in ("pa_reshape_and_cache", "pa_paged_attention_decode", "pa_paged_attention_prefill",
+              "pa_gather_kv", "pa_decode_workspace_bytes", "pa_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(pa.LIB_PATH)
+    missing = [n for n in _declared() if not hasattr(L, n)]
+    assert not missing
+
+
+def test_status_strings():
+    L = pa.lib()
+    for code in (0, -1, -2, -3, -4):
+        assert L.pa_status_string(code)
+    assert L.pa_status_string(5) == b"unknown status"
+
+
+NULL = ctypes.c_void_p(0)
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def _rc(**kw):
+    a = dict(k=FAKE, v=FAKE, kc=FAKE, vc=FAKE, slot=FAKE, T=4, H=2, D=128, bs=16, nb=8, dt=1)
+    a.update(kw)
+    return pa.lib().pa_reshape_and_cache(a["k"], a["v"], a["kc"], a["vc"], a["slot"], a["T"], a["H"], a["D"],
+                                         a["bs"], a["nb"], a["dt"], NULL)
+
+
+def test_reshape_and_cache_validation():
+    assert _rc(k=NULL) == pa.PA_ERR_INVALID_ARG
+    assert _rc(slot=NULL) == pa.PA_ERR_INVALID_ARG
+    assert _rc(T=-1) == pa.PA_ERR_INVALID_ARG
+    assert _rc(H=0) == pa.PA_ERR_INVALID_ARG
+    assert _rc(D=96) == pa.PA_ERR_UNSUPPORTED
+    assert _rc(bs=8) == pa.PA_ERR_UNSUPPORTED
+    assert _rc(dt=7) == pa.PA_ERR_UNSUPPORTED
+    assert _rc(nb=2 ** 28) == pa.PA_ERR_INVALID_ARG  # num_blocks * block_size overflows int32 slots
+    assert _rc(T=0, k=NULL, v=NULL, slot=NULL) == pa.PA_OK  # empty write is a no-op
+
+
+def _dec(fn="pa_paged_attention_decode", **kw):
+    a = dict(out=FAKE, odt=0, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, ctx=FAKE, S=4, H=2, Hkv=2, D=128, bs=16, nb=64,
+             maxb=8, maxctx=100, scale=0.1, dt=1, ws=NULL, wsb=0)
+    a.update(kw)
+    return getattr(pa.lib(), fn)(a["out"], a["odt"], a["q"], a["kc"], a["vc"], a["bt"], a["ctx"], a["S"], a["H"],
+                                 a["Hkv"], a["D"], a["bs"], a["nb"], a["maxb"], a["maxctx"], a["scale"], a["dt"],
+                                 a["ws"], a["wsb"], NULL)
+
+
+@pytest.mark.parametrize("fn", ["pa_paged_attention_decode", "pa_paged_attention_decode_partitions"])
+def test_decode_validation(fn):
+    assert _dec(fn, q=NULL) == pa.PA_ERR_INVALID_ARG
+    assert _dec(fn, bt=NULL) == pa.PA_ERR_INVALID_ARG
+    assert _dec(fn, Hkv=1) == pa.PA_ERR_UNSUPPORTED
+    assert _dec(fn, odt=2) == pa.PA_ERR_UNSUPPORTED  # bf16 out for f16 in
+    assert _dec(fn, D=80) == pa.PA_ERR_UNSUPPORTED
+    assert _dec(fn, bs=64) == pa.PA_ERR_UNSUPPORTED
+    assert _dec(fn, maxctx=8 * 16 + 1) == pa.PA_ERR_INVALID_ARG  # beyond max_blocks_per_seq * block_size
+    assert _dec(fn, scale=float("nan")) == pa.PA_ERR_INVALID_ARG
+    assert _dec(fn, S=-1) == pa.PA_ERR_INVALID_ARG
+    assert _dec(fn, S=0, q=NULL, out=NULL) == pa.PA_OK
+    # split-K needs a big enough, aligned workspace once contexts exceed one partition
+    P = pa.decode_partition_tokens()
+    need = pa.decode_workspace_bytes(4, 2, 128, 2 * P)
+    assert need == 4 * 2 * 2 * (128 + 2) * 4
+    assert _dec(fn, maxb=64, maxctx=2 * P, ws=FAKE, wsb=need - 4) == pa.PA_ERR_WORKSPACE
+    assert _dec(fn, maxb=64, maxctx=2 * P, ws=ctypes.c_void_p(0x1004), wsb=need) == pa.PA_ERR_WORKSPACE
+
+
+def test_workspace_size_rules():
+    P = pa.decode_partition_tokens()
+    assert P % 32 == 0
+    assert pa.decode_workspace_bytes(64, 32, 128, P) == 0  # one partition: no workspace
+    assert pa.decode_workspace_bytes(64, 32, 128, P + 1) == 64 * 32 * 2 * 130 * 4
+    assert pa.decode_workspace_bytes(0, 32, 128, 4096) == 0
+
+
+def _pf(**kw):
+    a = dict(out=FAKE, odt=0, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, ctx=FAKE, qsl=FAKE, S=2, TQ=10, maxq=6, H=2, Hkv=2,
+             D=128, bs=16, nb=64, maxb=8, maxctx=100, scale=0.1, dt=1)
+    a.update(kw)
+    return pa.lib().pa_paged_attention_prefill(a["out"], a["odt"], a["q"], a["kc"], a["vc"], a["bt"], a["ctx"],
+                                               a["qsl"], a["S"], a["TQ"], a["maxq"], a["H"], a["Hkv"], a["D"], a["bs"],
+                                               a["nb"], a["maxb"], a["maxctx"], a["scale"], a["dt"], NULL)
+
+
+def test_prefill_validation():
+    assert _pf(qsl=NULL) == pa.PA_ERR_INVALID_ARG
+    assert _pf(maxq=101) == pa.PA_ERR_INVALID_ARG  # a chunk longer than its context
+    assert _pf(TQ=13) == pa.PA_ERR_INVALID_ARG     # more rows than num_seqs * max_q_len
+    assert _pf(Hkv=4) == pa.PA_ERR_UNSUPPORTED
+    assert _pf(D=256) == pa.PA_ERR_UNSUPPORTED
+    assert _pf(dt=3) == pa.PA_ERR_UNSUPPORTED
+    assert _pf(TQ=0, q=NULL, out=NULL) == pa.PA_OK
+
+
+def test_gather_validation():
+    L = pa.lib()
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 100, 2, 128, 16, 64, 8, 1, NULL]
+    bad = list(args); bad[6] = NULL
+    assert L.pa_gather_kv(*bad) == pa.PA_ERR_INVALID_ARG
+    bad = list(args); bad[7] = 70000
+    assert L.pa_gather_kv(*bad) == pa.PA_ERR_INVALID_ARG
+    bad = list(args); bad[8] = 200
+    assert L.pa_gather_kv(*bad) == pa.PA_ERR_INVALID_ARG
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 2, 16, 64)
+    with pytest.raises(ValueError):
+        pa.reshape_and_cache(torch.zeros(1, 2, 64), torch.zeros(1, 2, 64), x, x, torch.zeros(1, dtype=torch.int32))

@@ -1,0 +1,234 @@
+"""GPU parity of the HIP library against the fp64 oracle, through the C ABI.
+
+Bars: bit-exact for the cache write and the block-table gather; for
+attention, max-abs error of the fp32 output <= 2e-3 (f16/bf16 inputs) or
+1e-5 (f32 inputs), and a narrowed output equal bit for bit to the
+round-to-nearest-even of the same kernel's fp32 output."""
+import functools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_391_amd as pa
+from tests._gpu import ATOL, TORCH_DT, OnDevice, bits, dev, host, rne
+from workloads import config4, decode_workload, make_config, prefill_workload
+
+pytestmark = pytest.mark.gpu
+
+
+@functools.lru_cache(maxsize=None)
+def _config(cid):
+    wl = make_config(cid)
+    kc, vc = oracle.reshape_and_cache(wl.new.k, wl.new.v, wl.k_cache, wl.v_cache, wl.new.slot_mapping,
+                                      wl.block_size, wl.dtype)
+    return wl, kc, vc
+
+
+def _on_device_written(wl):
+    od = OnDevice(wl)
+    od.write_new_tokens()
+    return od
+
+
+def _check_attention(got_f32: torch.Tensor, ref: np.ndarray, dtype: str):
+    got = host(got_f32).astype(np.float64)
+    assert got.shape == ref.shape
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref).max() if got.size else 0.0
+    assert err <= ATOL[dtype], f"max abs error {err:.3e} > {ATOL[dtype]}"
+    return err
+
+
+# ------------------------------------------------------------ cache writes
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_reshape_and_cache_bit_exact(cid):
+    wl, kc_ref, vc_ref = _config(cid)
+    od = _on_device_written(wl)
+    assert np.array_equal(bits(host(od.k_cache)), bits(kc_ref))
+    assert np.array_equal(bits(host(od.v_cache)), bits(vc_ref))
+
+
+@pytest.mark.parametrize("cid", [1, 3, 4])
+def test_gather_kv_bit_exact(cid):
+    wl, kc_ref, vc_ref = _config(cid)
+    od = _on_device_written(wl)
+    d = wl.decode
+    cu = np.concatenate([[0], np.cumsum(d.context_lens)]).astype(np.int32)
+    total = int(cu[-1])
+    k_out = torch.empty((total, wl.num_heads, wl.head_dim), dtype=TORCH_DT[wl.dtype], device="cuda")
+    v_out = torch.empty_like(k_out)
+    pa.gather_kv(k_out, v_out, od.k_cache, od.v_cache, od.block_tables, od.context_lens, dev(cu),
+                 d.max_context_len)
+    k_ref, v_ref = oracle.gather_kv(kc_ref, vc_ref, d.block_tables, d.context_lens, wl.dtype)
+    assert np.array_equal(bits(host(k_out)), bits(k_ref))
+    assert np.array_equal(bits(host(v_out)), bits(v_ref))
+
+
+# ------------------------------------------------------------------ decode
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_decode_parity_full_config(cid):
+    wl, kc_ref, vc_ref = _config(cid)
+    d = wl.decode
+    ref = oracle.decode(d.q, kc_ref, vc_ref, d.block_tables, d.context_lens, wl.scale, wl.dtype)
+    od = _on_device_written(wl)
+    out32 = od.decode(torch.float32)
+    err = _check_attention(out32, ref, wl.dtype)
+    print(f"config {cid} decode max abs err {err:.3e}")
+    if wl.dtype != "f32":
+        outn = od.decode(TORCH_DT[wl.dtype])
+        assert np.array_equal(bits(host(outn)), bits(rne(host(out32), wl.dtype)))
+
+
+def _ragged_cases():
+    cases = []
+    for dtype in ("f32", "f16", "bf16"):
+        for D in (64, 128):
+            for bs in (16, 32):
+                cases.append((dtype, D, bs))
+    return cases
+
+
+@pytest.mark.parametrize("dtype,D,bs", _ragged_cases())
+def test_decode_ragged_lengths(dtype, D, bs):
+    P = pa.decode_partition_tokens()
+    ctx = [1, 2, 15, 16, 17, 31, 33, 100, P - 1, P, P + 1, 2 * P + 7, 3 * P]
+    wl = decode_workload(f"ragged_{dtype}_{D}_{bs}", 500 + D + bs, dtype, 3, D, bs, ctx,
+                         maxb=math.ceil(max(ctx) / bs) + 2, pool_factor=1.3)
+    od = _on_device_written(wl)
+    kc, vc = oracle.reshape_and_cache(wl.new.k, wl.new.v, wl.k_cache, wl.v_cache, wl.new.slot_mapping, bs, dtype)
+    d = wl.decode
+    ref = oracle.decode(d.q, kc, vc, d.block_tables, d.context_lens, wl.scale, dtype)
+    _check_attention(od.decode(torch.float32, split=True), ref, dtype)
+    _check_attention(od.decode(torch.float32, split=False), ref, dtype)
+
+
+def test_decode_empty_context_gives_zeros():
+    wl = decode_workload("empty", 601, "f16", 2, 128, 16, [0, 5, 0, 40], maxb=4, pool_blocks=8)
+    od = _on_device_written(wl)
+    out = host(od.decode(torch.float32)).astype(np.float64)
+    assert np.all(out[[0, 2]] == 0.0)
+    assert np.isfinite(out).all()
+
+
+def test_decode_is_deterministic_and_stage_split_matches():
+    wl, _, _ = _config(3)
+    od = _on_device_written(wl)
+    a = host(od.decode(torch.float32))
+    b = host(od.decode(torch.float32))
+    assert np.array_equal(bits(a), bits(b))
+    d = wl.decode
+    out = torch.empty_like(od.q, dtype=torch.float32)
+    ws = pa.make_decode_workspace(d.num_seqs, wl.num_heads, wl.head_dim, d.max_context_len)
+    pa.paged_attention_decode_partitions(out, od.q, od.k_cache, od.v_cache, od.block_tables, od.context_lens,
+                                         wl.scale, d.max_context_len, ws)
+    pa.paged_attention_decode_reduce(out, od.context_lens, wl.head_dim, d.max_context_len, od.q.dtype, ws)
+    assert np.array_equal(bits(host(out)), bits(a))
+
+
+def test_decode_single_partition_is_bit_identical_with_or_without_workspace():
+    P = pa.decode_partition_tokens()
+    wl = decode_workload("onepart", 602, "bf16", 4, 128, 32, [7, P // 2, P - 3, P], maxb=P // 32, pool_factor=1.2)
+    od = _on_device_written(wl)
+    assert np.array_equal(bits(host(od.decode(split=True))), bits(host(od.decode(split=False))))
+
+
+def test_decode_bit_identical_under_block_permutation():
+    wl, _, _ = _config(2)
+    od = _on_device_written(wl)
+    base = host(od.decode(torch.float32))
+    g = torch.Generator(device="cpu").manual_seed(5)
+    perm = torch.randperm(wl.num_blocks, generator=g).to("cuda")  # block b moves to perm[b]
+    kc = torch.empty_like(od.k_cache)
+    vc = torch.empty_like(od.v_cache)
+    kc[perm] = od.k_cache
+    vc[perm] = od.v_cache
+    bt = od.block_tables.clone()
+    valid = bt >= 0
+    bt[valid] = perm[bt[valid].long()].int()
+    out = host(od.decode(torch.float32, block_tables=bt, k_cache=kc, v_cache=vc))
+    assert np.array_equal(bits(out), bits(base))
+
+
+def test_decode_bit_identical_with_aliased_or_private_prefix_blocks():
+    wl = config4(prompts=4, samples=8, prompt_len=256, max_tail=64, cow=True)
+    od = _on_device_written(wl)
+    base = host(od.decode(torch.float32))
+    bt = wl.decode.block_tables.copy()
+    refs = wl.notes["refcount"]
+    extra_src = []
+    nb = wl.num_blocks
+    for s in range(bt.shape[0]):
+        for i in range(bt.shape[1]):
+            if bt[s, i] >= 0 and refs[bt[s, i]] > 1:
+                extra_src.append(int(bt[s, i]))
+                bt[s, i] = nb
+                nb += 1
+    src = torch.tensor(extra_src, device="cuda", dtype=torch.long)
+    kc = torch.cat([od.k_cache, od.k_cache[src]])
+    vc = torch.cat([od.v_cache, od.v_cache[src]])
+    out = host(od.decode(torch.float32, block_tables=dev(bt), k_cache=kc, v_cache=vc))
+    assert np.array_equal(bits(out), bits(base))
+    # and against the oracle on the aliased layout
+    kc_ref, vc_ref = oracle.reshape_and_cache(wl.new.k, wl.new.v, wl.k_cache, wl.v_cache, wl.new.slot_mapping, 16,
+                                              "f16")
+    d = wl.decode
+    ref = oracle.decode(d.q, kc_ref, vc_ref, d.block_tables, d.context_lens, wl.scale, "f16")
+    assert np.abs(base.astype(np.float64) - ref).max() <= ATOL["f16"]
+
+
+# ----------------------------------------------------------------- prefill
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("bs", [16, 32])
+def test_prefill_parity_small_chunks(dtype, bs):
+    prior = [0, 5, 33, 100, 0, 300]
+    chunk = [1, 17, 64, 130, 200, 77]
+    maxb = math.ceil(max(p + c for p, c in zip(prior, chunk)) / bs)
+    wl = prefill_workload(f"pf_{dtype}_{bs}", 700 + bs, dtype, 4, 128, bs, prior, chunk, maxb=maxb, pool_factor=1.2)
+    od = _on_device_written(wl)
+    kc, vc = oracle.reshape_and_cache(wl.new.k, wl.new.v, wl.k_cache, wl.v_cache, wl.new.slot_mapping, bs, dtype)
+    p = wl.prefill
+    ref = oracle.prefill(p.q, kc, vc, p.block_tables, p.context_lens, p.query_start_loc, wl.scale, dtype)
+    out32 = od.prefill(torch.float32)
+    tol = ATOL[dtype]
+    got = host(out32).astype(np.float64)
+    err = np.abs(got - ref).max()
+    assert err <= tol, f"prefill max abs err {err:.3e}"
+    if dtype != "f32":
+        outn = od.prefill(TORCH_DT[dtype])
+        assert np.array_equal(bits(host(outn)), bits(rne(host(out32), dtype)))
+
+
+def test_prefill_config5_sampled_rows_and_decode():
+    wl, kc_ref, vc_ref = _config(5)
+    od = _on_device_written(wl)
+    p = wl.prefill
+    out = host(od.prefill(torch.float32)).astype(np.float64)
+    rng = np.random.default_rng(0)
+    rows = rng.integers(0, p.total_q, size=1500)
+    ends = np.concatenate([p.query_start_loc[:-1], p.query_start_loc[1:] - 1])
+    rows = np.concatenate([rows, ends])
+    heads = rng.integers(0, wl.num_heads, size=rows.shape[0])
+    pairs = np.stack([rows, heads], 1)
+    ref = oracle.prefill(p.q, kc_ref, vc_ref, p.block_tables, p.context_lens, p.query_start_loc, wl.scale, wl.dtype,
+                         rows=pairs)
+    err = np.abs(out[rows, heads] - ref).max()
+    print(f"config 5 prefill sampled max abs err {err:.3e}")
+    assert err <= ATOL[wl.dtype]
+
+
+def test_prefill_single_query_chunk_matches_decode():
+    ctx = [1, 40, 300, 1000]
+    wl = prefill_workload("pf1", 704, "f16", 4, 128, 16, [c - 1 for c in ctx], [1] * 4, maxb=64)
+    od = _on_device_written(wl)
+    p = wl.prefill
+    pf = host(od.prefill(torch.float32)).astype(np.float64)
+    out = torch.empty((4, 4, 128), dtype=torch.float32, device="cuda")
+    pa.paged_attention_decode(out, od.pf_q, od.k_cache, od.v_cache, od.pf_block_tables, od.pf_context_lens,
+                              wl.scale, max_context_len=p.max_context_len)
+    assert np.abs(pf - host(out).astype(np.float64)).max() <= 2 * ATOL["f16"]
