@@ -1,28 +1,330 @@
-// Causal prefill of query chunks (placeholder: vector path per query row).
+// Causal prefill of multi-token query chunks over the paged cache, on MFMA.
+//
+// A chunk of L new tokens of a sequence attends to the sequence's cached
+// tokens through its block table (devpress.csdn.net page, sections on how
+// PagedAttention works and on the paged KV cache; betteryeah.com page,
+// section 2.4); the chunk's own K/V are already cached and it is the last L
+// of ctx tokens, so query j (position ctx-L+j) sees tokens 0..ctx-L+j.
+//
+// With many queries per key this is a dense contraction, so it runs on the
+// gfx950 matrix cores (v_mfma_f32_16x16x32_{f16,bf16}, fp32 accumulate).
+// Orientation: the wave computes S^T = K Q^T (keys on the MFMA rows, its
+// queries on the columns) and O^T += V^T P^T. In that orientation the
+// score accumulator a lane holds (one query, four keys per 16-key subtile)
+// is exactly the B operand P^T needs, so P never leaves registers; the
+// price is a transposed V tile, which the workgroup writes into LDS while
+// staging it. Per 64-key tile:
+//   * 256 threads gather the K tile (row-major) and V tile (transposed)
+//     through the block table into LDS; the next tile's global loads are
+//     issued before the current tile's math, so they overlap it;
+//   * each wave owns 32 queries (two 16-query groups); every K or V^T
+//     fragment read from LDS feeds both groups' MFMAs;
+//   * online softmax per query: in-lane max/sum over the lane's keys plus
+//     two cross-row shuffles; tiles past a wave's last query are skipped and
+//     only the diagonal tiles carry a mask.
+// P is rounded to the input type for the P.V product; for bf16 it is split
+// into a bf16 head and a bf16 remainder (two MFMAs) to keep ~16 bits.
 #include "pa_internal.h"
 
 namespace pa {
 
-int prefill_mfma_q_tile() { return 128; }
+namespace {
 
-hipError_t launch_prefill_mfma(const PrefillArgs& p, Dt dt, int D, int BS, hipStream_t stream) {
-  DecodeArgs a{};
-  a.out = p.out;
-  a.q = p.q;
-  a.k_cache = p.k_cache;
-  a.v_cache = p.v_cache;
-  a.block_tables = p.block_tables;
-  a.context_lens = p.context_lens;
-  a.query_start_loc = p.query_start_loc;
-  a.num_seqs = p.num_seqs;
-  a.num_rows = p.total_q;
-  a.H = p.H;
-  a.max_blocks = p.max_blocks;
-  a.max_parts = 1;
-  a.part_tiles = (p.max_context_len + 15) / 16;
-  a.scale_log2 = p.scale_log2;
-  a.out_f32 = p.out_f32;
-  return launch_decode_partitions(a, dt, D, BS, true, stream);
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int KT = 64;       // keys per tile
+constexpr int NQ = 2;        // 16-query groups per wave
+constexpr int QW = 16 * NQ;  // queries per wave
+constexpr int QT = 4 * QW;   // queries per workgroup
+
+template <Dt DT> __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (DT == Dt::F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+
+// 16-bit bits of x in the input type (round to nearest even)
+template <Dt DT> __device__ __forceinline__ uint32_t to_bits(float x) {
+  if constexpr (DT == Dt::F16) return f32_to_f16_bits(x);
+  else return f32_to_bf16_bits(x);
+}
+template <Dt DT> __device__ __forceinline__ float from_bits(uint32_t b) {
+  if constexpr (DT == Dt::F16) return f16_bits_to_f32(b);
+  else return bf16_bits_to_f32(b);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+}  // namespace
+
+template <Dt DT, int D, int BS>
+__global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) {
+  constexpr int KS = D / 32;     // MFMA k-steps over head_dim for Q.K
+  constexpr int NDT = D / 16;    // 16-row tiles of O^T
+  constexpr int CPR = D / 8;     // 16-byte chunks per K/V row
+  constexpr int KROW = D + 8;    // K tile row stride in LDS (halves), padded against bank conflicts
+  constexpr int VROW = KT + 4;   // V^T tile row stride in LDS (halves)
+  constexpr int KCH = KT * CPR / 256;        // K chunks per thread
+  constexpr int VPR = (KT / 2) * CPR / 256;  // V key-pairs x chunks per thread
+  static_assert(KCH >= 1 && VPR >= 1, "tile too small for the workgroup");
+
+  __shared__ __align__(16) uint16_t sk[KT * KROW];
+  __shared__ __align__(16) uint16_t sv[D * VROW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n16 = lane & 15;
+  const int g4 = lane >> 4;
+
+  int bid = blockIdx.x;
+  const int h = bid % a.H;
+  bid /= a.H;
+  const int s = bid % a.num_seqs;
+  bid /= a.num_seqs;
+  const int qt = a.q_tiles - 1 - bid;  // latest (heaviest) query tiles are dispatched first
+  const int q_beg = a.query_start_loc[s];
+  const int L = a.query_start_loc[s + 1] - q_beg;
+  const int j0 = qt * QT;
+  if (j0 >= L) return;
+  const int ctx = a.context_lens[s];
+  const int c0 = ctx - L;                          // position of the chunk's first query
+  const int kv_end = c0 + min(j0 + QT, L);         // keys this workgroup needs: [0, kv_end)
+  const int n_tiles = (kv_end + KT - 1) / KT;
+  const int wq0 = j0 + wave * QW;                  // the wave's first query (chunk-relative)
+  const bool wave_active = wq0 < L;
+  const int wave_last_pos = c0 + min(wq0 + QW, L) - 1;
+
+  const char* kc = reinterpret_cast<const char*>(a.k_cache);
+  const char* vc = reinterpret_cast<const char*>(a.v_cache);
+  const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks;
+
+  // Q^T fragments (B operand of S^T = K Q^T): query n16 of group g, d = 32*ks + 8*g4 .. +7
+  u32x4 qf[NQ][KS];
+#pragma unroll
+  for (int g = 0; g < NQ; ++g) {
+    const int jq = wq0 + g * 16 + n16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (jq < L) {
+        const char* p = reinterpret_cast<const char*>(a.q) + (((int64_t)(q_beg + jq) * a.H + h) * D + ks * 32 + 8 * g4) * 2;
+        qf[g][ks] = *reinterpret_cast<const u32x4*>(p);
+      } else {
+        qf[g][ks] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+
+  f32x4 o[NQ][NDT];
+  float m[NQ], l[NQ];
+#pragma unroll
+  for (int g = 0; g < NQ; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[g][dt] = zero4();
+  }
+
+  // ---- global -> registers for one tile (zeros past kv_end)
+  u32x4 kreg[KCH], vreg[2 * VPR];
+  auto fetch = [&](int t) {
+    const int kv0 = t * KT;
+#pragma unroll
+    for (int r = 0; r < KCH; ++r) {
+      const int ci = tid + 256 * r;
+      const int key = ci / CPR, dc = ci % CPR;
+      const int pos = kv0 + key;
+      kreg[r] = u32x4{0u, 0u, 0u, 0u};
+      if (pos < kv_end) {
+        const int32_t phys = bt_row[pos / BS];
+        kreg[r] = *reinterpret_cast<const u32x4*>(kc + kv_row_offset(phys, h, pos % BS, a.H, BS, D) * 2 + dc * 16);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < VPR; ++r) {
+      const int pi = tid + 256 * r;
+      const int kp = pi / CPR, dc = pi % CPR;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int pos = kv0 + 2 * kp + e;
+        vreg[2 * r + e] = u32x4{0u, 0u, 0u, 0u};
+        if (pos < kv_end) {
+          const int32_t phys = bt_row[pos / BS];
+          vreg[2 * r + e] =
+              *reinterpret_cast<const u32x4*>(vc + kv_row_offset(phys, h, pos % BS, a.H, BS, D) * 2 + dc * 16);
+        }
+      }
+    }
+  };
+  // ---- registers -> LDS: K row-major, V transposed (two keys packed per word)
+  auto stage = [&]() {
+#pragma unroll
+    for (int r = 0; r < KCH; ++r) {
+      const int ci = tid + 256 * r;
+      const int key = ci / CPR, dc = ci % CPR;
+      *reinterpret_cast<u32x4*>(&sk[key * KROW + dc * 8]) = kreg[r];
+    }
+#pragma unroll
+    for (int r = 0; r < VPR; ++r) {
+      const int pi = tid + 256 * r;
+      const int kp = pi / CPR, dc = pi % CPR;
+      const u32x4 v0 = vreg[2 * r], v1 = vreg[2 * r + 1];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t lo = (v0[w] & 0xffffu) | (v1[w] << 16);          // element 2w of keys 2kp, 2kp+1
+        const uint32_t hi = (v0[w] >> 16) | (v1[w] & 0xffff0000u);      // element 2w+1
+        *reinterpret_cast<uint32_t*>(&sv[(dc * 8 + 2 * w) * VROW + 2 * kp]) = lo;
+        *reinterpret_cast<uint32_t*>(&sv[(dc * 8 + 2 * w + 1) * VROW + 2 * kp]) = hi;
+      }
+    }
+  };
+
+  fetch(0);
+  for (int t = 0; t < n_tiles; ++t) {
+    const int kv0 = t * KT;
+    __syncthreads();  // everyone is done reading the previous tile
+    stage();
+    __syncthreads();
+    if (t + 1 < n_tiles) fetch(t + 1);  // in flight during this tile's math
+
+    if (wave_active && kv0 <= wave_last_pos) {
+      // S^T = K Q^T for 4 key subtiles of 16
+      f32x4 sacc[NQ][4];
+#pragma unroll
+      for (int g = 0; g < NQ; ++g)
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub) sacc[g][sub] = zero4();
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4 ka = *reinterpret_cast<const u32x4*>(&sk[(sub * 16 + n16) * KROW + ks * 32 + 8 * g4]);
+#pragma unroll
+          for (int g = 0; g < NQ; ++g) sacc[g][sub] = mfma<DT>(ka, qf[g][ks], sacc[g][sub]);
+        }
+      }
+      // online softmax; lane holds query n16, keys kv0 + 16*sub + 4*g4 + i
+      u32x4 pb[NQ][2];
+      u32x4 pbl[NQ][2];  // bf16 remainders
+#pragma unroll
+      for (int g = 0; g < NQ; ++g) {
+        const int qpos = c0 + wq0 + g * 16 + n16;
+        const int last_key = min(qpos, kv_end - 1);
+        float sc[16];
+        float mt = -INFINITY;
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kv0 + 16 * sub + 4 * g4 + i;
+            const float x = sacc[g][sub][i] * a.scale_log2;
+            sc[4 * sub + i] = key <= last_key ? x : -INFINITY;
+            mt = fmaxf(mt, sc[4 * sub + i]);
+          }
+        mt = fmaxf(mt, shfl_xor_f(mt, 16));
+        mt = fmaxf(mt, shfl_xor_f(mt, 32));
+        const float m_new = fmaxf(m[g], mt);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m[g] - m_use);
+        float psum = 0.f;
+        uint32_t ph[16], pl[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = __builtin_amdgcn_exp2f(sc[i] - m_use);
+          psum += p;
+          ph[i] = to_bits<DT>(p);
+          pl[i] = DT == Dt::BF16 ? to_bits<DT>(p - from_bits<DT>(ph[i])) : 0u;
+        }
+        l[g] = l[g] * alpha + psum;
+        m[g] = m_new;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[g][dt] *= alpha;
+        // B operand of O^T += V^T P^T for key step kst: elements 0..3 from
+        // subtile 2*kst, 4..7 from subtile 2*kst+1
+#pragma unroll
+        for (int kst = 0; kst < 2; ++kst) {
+          const int b0 = 8 * kst;
+          pb[g][kst] = u32x4{ph[b0] | (ph[b0 + 1] << 16), ph[b0 + 2] | (ph[b0 + 3] << 16),
+                             ph[b0 + 4] | (ph[b0 + 5] << 16), ph[b0 + 6] | (ph[b0 + 7] << 16)};
+          pbl[g][kst] = u32x4{pl[b0] | (pl[b0 + 1] << 16), pl[b0 + 2] | (pl[b0 + 3] << 16),
+                              pl[b0 + 4] | (pl[b0 + 5] << 16), pl[b0 + 6] | (pl[b0 + 7] << 16)};
+        }
+      }
+      // O^T += V^T P^T: A = V^T rows d = 16*dt + n16, keys 32*kst + 4*g4 + {0..3} and +16
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+        for (int kst = 0; kst < 2; ++kst) {
+          const uint16_t* row = &sv[(dt * 16 + n16) * VROW + kst * 32 + 4 * g4];
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(row);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 16);
+          const u32x4 va = u32x4{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+          for (int g = 0; g < NQ; ++g) {
+            o[g][dt] = mfma<DT>(va, pb[g][kst], o[g][dt]);
+            if constexpr (DT == Dt::BF16) o[g][dt] = mfma<DT>(va, pbl[g][kst], o[g][dt]);
+          }
+        }
+      }
+    }
+  }
+
+  if (!wave_active) return;
+  // finish: l summed over the four lane rows that share a query
+#pragma unroll
+  for (int g = 0; g < NQ; ++g) {
+    float lt = l[g] + shfl_xor_f(l[g], 16);
+    lt += shfl_xor_f(lt, 32);
+    const int jq = wq0 + g * 16 + n16;
+    if (jq >= L) continue;
+    const int64_t orow = ((int64_t)(q_beg + jq) * a.H + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int d0 = dt * 16 + 4 * g4;
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = o[g][dt][i] / lt;
+      if (a.out_f32) {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + orow + d0) = f32x4{v[0], v[1], v[2], v[3]};
+      } else {
+        const uint32_t w0 = to_bits<DT>(v[0]) | (to_bits<DT>(v[1]) << 16);
+        const uint32_t w1 = to_bits<DT>(v[2]) | (to_bits<DT>(v[3]) << 16);
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + orow + d0) = u32x2{w0, w1};
+      }
+    }
+  }
+}
+
+int prefill_mfma_q_tile() { return QT; }
+
+template <Dt DT, int D, int BS>
+static hipError_t launch_k4(const PrefillArgs& a, hipStream_t stream) {
+  const int64_t grid = (int64_t)a.q_tiles * a.num_seqs * a.H;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((prefill_mfma_kernel<DT, D, BS>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <Dt DT>
+static hipError_t dispatch_k4(const PrefillArgs& a, int D, int BS, hipStream_t stream) {
+  if (D == 128 && BS == 16) return launch_k4<DT, 128, 16>(a, stream);
+  if (D == 128 && BS == 32) return launch_k4<DT, 128, 32>(a, stream);
+  if (D == 64 && BS == 16) return launch_k4<DT, 64, 16>(a, stream);
+  if (D == 64 && BS == 32) return launch_k4<DT, 64, 32>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_mfma(const PrefillArgs& a, Dt dt, int D, int BS, hipStream_t stream) {
+  if (dt == Dt::F16) return dispatch_k4<Dt::F16>(a, D, BS, stream);
+  if (dt == Dt::BF16) return dispatch_k4<Dt::BF16>(a, D, BS, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pa
