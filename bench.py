@@ -7,7 +7,9 @@ random permutation of a pool sized to fit exactly, q/K/V ~ N(0,1).
 
 One step = one decode iteration of one attention layer, all inputs resident
 in HBM: reshape_and_cache of the 64 new tokens, then split-K decode
-(partition kernel + reduction kernel) with an f16 output.
+(partition kernel + reduction kernel) with an f16 output. The timed steps
+replay the step captured as a HIP graph (checked bit-identical to the eager
+step); --eager times plain launches instead.
 
 Prints ONE JSON line: value = algorithmic bytes of the step / step time
 (GB/s, 1e9 B/s); roofline = the partition kernel's algorithmic bytes over its
@@ -43,14 +45,62 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _counter_rows(path):
+    """(kernel name, counter value) per dispatch from a rocprofv3 counter
+    collection CSV (one counter per run)."""
+    import csv
+    import glob
+    files = [path] if path.endswith(".csv") else glob.glob(os.path.join(path, "**", "*counter_collection.csv"),
+                                                              recursive=True)
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def record_traffic(fetch_dir, write_dir, copy_bytes):
+    """Turn two counter runs of this benchmark (FETCH_SIZE, then WRITE_SIZE;
+    both in KiB per dispatch) into HBM bytes per launch of the partition
+    kernel, each scaled by what the same counter reads for the plain device
+    copy of known size in the same run, and store them with the hash of the
+    kernel source they describe."""
+    out = {}
+    for name, d in (("fetch", fetch_dir), ("write", write_dir)):
+        rows = _counter_rows(d)
+        part = [v for k, v in rows if "decode_partition_kernel" in k]
+        copy = [v for k, v in rows if "copyBuffer" in k or "copy" in k.lower()]
+        copy = max(copy)  # the 1 GiB probe copy is the largest copy dispatch
+        scale = (copy_bytes / 1024.0) / copy
+        out[name] = {"partition_kernel_kib_avg": sum(part) / len(part), "copy_kib": copy, "scale": scale,
+                     "dispatches": len(part)}
+    fetch = out["fetch"]["partition_kernel_kib_avg"] * 1024 * out["fetch"]["scale"]
+    write = out["write"]["partition_kernel_kib_avg"] * 1024 * out["write"]["scale"]
+    rec = {"kernel": "decode_partition_kernel<f16,128,16>", "workload": "llama7b decode (bench.py)",
+           "kernel_source_sha256": kernel_source_hash(), "hbm_bytes_per_launch": round(fetch + write),
+           "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write), "counters": out}
+    import paged_kv_cache_391_amd as pa
+    rec["partition_tokens"] = pa.decode_partition_tokens()
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--copy-probe-gib", type=float, default=1.0, help="size of the plain-copy bandwidth probe")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="store HBM bytes per launch from two rocprofv3 --pmc runs of this script and exit")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(args.record_traffic[0], args.record_traffic[1], int(args.copy_probe_gib * (1 << 30)))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         log("bench.py measures one GPU only: each GPU would run this path on its own share of sequences or "
             "heads with no collective in the timed region, so only --gpus 1 is measured.")
@@ -102,6 +152,7 @@ def main():
     decode_bytes = kv_bytes + table_bytes + qo_bytes
     step_bytes = decode_bytes + cache_write_bytes
 
+    # eager pass: HIP events on the launch stream around every partition-kernel launch
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -111,14 +162,44 @@ def main():
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
+    eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     k2_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     k3_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    eager_out = out.clone()
+
+    # timed pass: the step captured once as a HIP graph and replayed, as a
+    # serving loop runs decode (no host launch gaps between the 3 kernels)
+    ms_per_step = eager_ms
+    graph_ok = None
+    if not args.eager:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph_ok = True
+        for _ in range(max(1, args.warmup)):
+            out.zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+            graph_ok = graph_ok and bool(torch.equal(out, eager_out))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        graph_ok = graph_ok and bool(torch.equal(out, eager_out))
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     k2_gbps = k2_bytes / (k2_ms * 1e-3) / 1e9
-    log(f"[bench] {ms_per_step * 1e3:.1f} us/step, partition kernel {k2_ms * 1e3:.1f} us "
-        f"({k2_gbps:.0f} GB/s), reduction {k3_ms * 1e3:.1f} us")
+    log(f"[bench] {ms_per_step * 1e3:.1f} us/step ({'graph' if not args.eager else 'eager'}; eager "
+        f"{eager_ms * 1e3:.1f} us), partition kernel {k2_ms * 1e3:.1f} us ({k2_gbps:.0f} GB/s), "
+        f"reduction {k3_ms * 1e3:.1f} us, graph output == eager: {graph_ok}")
+    if graph_ok is False:
+        raise SystemExit("graph replay disagrees with the eager step")
 
     # ---- plain device copy: measured bandwidth next to the spec peak
     n = int(args.copy_probe_gib * (1 << 30)) // 4
@@ -176,6 +257,8 @@ def main():
                      "frac": round(k2_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "decode_partition_kernel<f16,128,16>", "bytes_per_launch": k2_bytes,
                      "avg_launch_us": round(k2_ms * 1e3, 2)},
+        "timing": "hip_graph_replay" if not args.eager else "eager",
+        "eager_ms_per_step": round(eager_ms, 5),
         "hbm_copy_probe_GBps": round(copy_gbps, 1),
         "step_bytes": step_bytes,
         "reduce_kernel_avg_us": round(k3_ms * 1e3, 2),

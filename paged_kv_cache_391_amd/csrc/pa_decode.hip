@@ -9,6 +9,10 @@
 //
 // Decode moves ~1 byte per flop, so it is bound by HBM bandwidth and uses no
 // matrix cores. Mapping (wave64):
+//   * a workgroup takes one partition of one sequence for a group of heads,
+//     one wave per head; the waves read neighbouring (block, head) tiles, so
+//     the group streams contiguous runs of each block, and the partitions are
+//     dispatched partition-major (every sequence's first partition first);
 //   * a wave streams 16-token tiles; one 16-lane row of the wave holds one
 //     token's K (or V) row, each lane 1/16 of it, so a load instruction
 //     reads 4 whole rows = 4 * D * elt contiguous bytes (1 KiB at d=128 f16);
@@ -174,8 +178,8 @@ __device__ __forceinline__ void prefill_row(const int32_t* qsl, const int32_t* c
 
 }  // namespace
 
-template <Dt DT, int D, int BS, int NW, bool PF>
-__global__ __launch_bounds__(NW * 64) void decode_partition_kernel(const DecodeArgs a) {
+template <Dt DT, int D, int BS, int HG, bool PF>
+__global__ __launch_bounds__(HG * 64) void decode_partition_kernel(const DecodeArgs a) {
   using L = Lane<DT, D>;
   constexpr int WPL = L::WPL;
   constexpr int TPB = BS / 16;  // tiles per block
@@ -185,11 +189,15 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(const DecodeA
   const int g = lane >> 4;
   const int c = lane & 15;
 
+  // grid: partition-major, then row, then head group; wave w takes head hg*HG + w
+  const int n_hg = (a.H + HG - 1) / HG;
   int bid = blockIdx.x;
-  const int part = bid % a.max_parts;
-  bid /= a.max_parts;
-  const int h = bid % a.H;
-  const int row = bid / a.H;
+  const int hg = bid % n_hg;
+  bid /= n_hg;
+  const int row = bid % a.num_rows;
+  const int part = bid / a.num_rows;
+  const int h = hg * HG + wave;
+  if (h >= a.H) return;
 
   int seq, ctx;
   if constexpr (PF) {
@@ -200,11 +208,10 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(const DecodeA
   }
   const int n_tiles = (ctx + 15) >> 4;
   const int nparts = (n_tiles + a.part_tiles - 1) / a.part_tiles;
-  if (part >= (nparts > 1 ? nparts : 1)) return;  // whole workgroup leaves together
+  if (part >= (nparts > 1 ? nparts : 1)) return;
 
   const int u0 = part * a.part_tiles;
-  const int u1 = min(n_tiles, u0 + a.part_tiles);
-  const int my_tiles = u1 - u0 > wave ? (u1 - u0 - wave + NW - 1) / NW : 0;
+  const int my_tiles = max(0, min(n_tiles, u0 + a.part_tiles) - u0);
 
   uint32_t qw[WPL];
   L::load(qw, reinterpret_cast<const char*>(a.q) + ((int64_t)row * a.H + h) * L::ROW_BYTES, (uint32_t)(c * L::VB));
@@ -223,13 +230,13 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(const DecodeA
 
   for (int base = 0; base < my_tiles; base += 64) {
     const int cnt = min(64, my_tiles - base);
-    // table entry of this wave's tile (base + lane)
+    // table entry of tile u0 + base + lane
     int32_t tb = 0;
-    if (lane < cnt) tb = bt_row[(u0 + wave + (base + lane) * NW) / TPB];
+    if (lane < cnt) tb = bt_row[(u0 + base + lane) / TPB];
 
     // wave-uniform byte offset of tile i's first row (K and V share it)
     auto tile_off = [&](int i, int& t0) -> int64_t {
-      const int u = u0 + wave + (base + i) * NW;
+      const int u = u0 + base + i;
       const int32_t phys = __builtin_amdgcn_readlane(tb, i);
       t0 = u * 16;
       return kv_row_offset(phys, h, (u % TPB) * 16, a.H, BS, D) * L::EB;
@@ -277,49 +284,13 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(const DecodeA
     }
     st.m = m_all;
   }
-
-  if constexpr (NW > 1) {
-    __shared__ float sm_acc[NW][D];
-    __shared__ float sm_ml[NW][2];
-    if (g == 0) {
-#pragma unroll
-      for (int k = 0; k < L::EPL; ++k) sm_acc[wave][L::elem(c, k)] = st.acc[k];
-      if (c == 0) {
-        sm_ml[wave][0] = st.m;
-        sm_ml[wave][1] = st.l;
-      }
-    }
-    __syncthreads();
-    if (wave != 0) return;
-    float M = sm_ml[0][0];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_ml[w][0]);
-    const float M_use = M == -INFINITY ? 0.f : M;
-    float fw[NW];
-    float Lsum = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      fw[w] = fast_exp2(sm_ml[w][0] - M_use);
-      Lsum += sm_ml[w][1] * fw[w];
-    }
-#pragma unroll
-    for (int k = 0; k < L::EPL; ++k) {
-      float x = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) x += sm_acc[w][L::elem(c, k)] * fw[w];
-      st.acc[k] = x;
-    }
-    st.m = M;
-    st.l = Lsum;
-  }
   if (g != 0) return;
 
   const int64_t orow = ((int64_t)row * a.H + h) * D;
   if (nparts <= 1) {
-    const float inv_ok = st.l > 0.f ? 1.f : 0.f;
 #pragma unroll
     for (int k = 0; k < L::EPL; ++k) {
-      const float o = inv_ok != 0.f ? st.acc[k] / st.l : 0.f;
+      const float o = st.l > 0.f ? st.acc[k] / st.l : 0.f;
       store_out<DT>(a.out, orow + L::elem(c, k), o, a.out_f32);
     }
   } else {
@@ -369,10 +340,11 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(const DecodeArgs a) {
 
 template <Dt DT, int D, int BS, bool PF>
 static hipError_t launch_k2(const DecodeArgs& a, hipStream_t stream) {
-  const int64_t grid = (int64_t)a.num_rows * a.H * a.max_parts;
+  const int64_t n_hg = (a.H + kDecodeHeadsPerGroup - 1) / kDecodeHeadsPerGroup;
+  const int64_t grid = (int64_t)a.num_rows * n_hg * a.max_parts;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((decode_partition_kernel<DT, D, BS, kDecodeWaves, PF>), dim3((unsigned)grid),
-                     dim3(kDecodeWaves * 64), 0, stream, a);
+  hipLaunchKernelGGL((decode_partition_kernel<DT, D, BS, kDecodeHeadsPerGroup, PF>), dim3((unsigned)grid),
+                     dim3(kDecodeHeadsPerGroup * 64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -7,9 +7,10 @@
 
 #include "pa_device.h"
 
-// Decode tuning: waves per workgroup and tokens per split-K partition.
-#ifndef PA_DECODE_WAVES
-#define PA_DECODE_WAVES 4
+// Decode tuning: heads per workgroup (one wave each) and tokens per split-K
+// partition.
+#ifndef PA_DECODE_HEADS
+#define PA_DECODE_HEADS 1
 #endif
 #ifndef PA_PARTITION_TOKENS
 #define PA_PARTITION_TOKENS 512
@@ -17,7 +18,7 @@
 
 namespace pa {
 
-constexpr int kDecodeWaves = PA_DECODE_WAVES;
+constexpr int kDecodeHeadsPerGroup = PA_DECODE_HEADS;
 constexpr int kPartitionTokens = PA_PARTITION_TOKENS;
 static_assert(kPartitionTokens % 32 == 0, "partitions must hold whole 16- and 32-token blocks");
 

@@ -13,12 +13,13 @@
 // score accumulator a lane holds (one query, four keys per 16-key subtile)
 // is exactly the B operand P^T needs, so P never leaves registers; the
 // price is a transposed V tile, which the workgroup writes into LDS while
-// staging it. Per 64-key tile:
-//   * 256 threads gather the K tile (row-major) and V tile (transposed)
-//     through the block table into LDS; the next tile's global loads are
-//     issued before the current tile's math, so they overlap it;
-//   * each wave owns 32 queries (two 16-query groups); every K or V^T
-//     fragment read from LDS feeds both groups' MFMAs;
+// staging it. Per tile of KT keys (32 or 64):
+//   * the workgroup stages the sequence's block-table row in LDS once, then
+//     256 threads gather each K tile (row-major) and V tile (transposed)
+//     through it into one of two LDS buffers; the next tile's global loads
+//     are in flight while the current tile is computed, one barrier per tile;
+//   * each wave owns NQ groups of 16 queries; every K or V^T fragment read
+//     from LDS feeds one MFMA per group;
 //   * online softmax per query: in-lane max/sum over the lane's keys plus
 //     two cross-row shuffles; tiles past a wave's last query are skipped and
 //     only the diagonal tiles carry a mask.
@@ -36,10 +37,18 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int KT = 64;       // keys per tile
-constexpr int NQ = 2;        // 16-query groups per wave
-constexpr int QW = 16 * NQ;  // queries per wave
-constexpr int QT = 4 * QW;   // queries per workgroup
+#ifndef PA_PREFILL_KT
+#define PA_PREFILL_KT 32
+#endif
+#ifndef PA_PREFILL_NQ
+#define PA_PREFILL_NQ 1
+#endif
+constexpr int KT = PA_PREFILL_KT;  // keys per tile (32 or 64)
+constexpr int NQ = PA_PREFILL_NQ;  // 16-query groups per wave
+constexpr int QW = 16 * NQ;        // queries per wave
+constexpr int QT = 4 * QW;         // queries per workgroup
+constexpr int MAXB_LDS = 512;      // block-table entries staged in LDS
+static_assert(KT == 32 || KT == 64, "key tile must be 32 or 64");
 
 template <Dt DT> __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
   if constexpr (DT == Dt::F16)
@@ -68,15 +77,19 @@ template <Dt DT, int D, int BS>
 __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) {
   constexpr int KS = D / 32;     // MFMA k-steps over head_dim for Q.K
   constexpr int NDT = D / 16;    // 16-row tiles of O^T
+  constexpr int NSUB = KT / 16;  // 16-key subtiles of S^T
+  constexpr int NKST = KT / 32;  // MFMA k-steps over keys for P.V
   constexpr int CPR = D / 8;     // 16-byte chunks per K/V row
   constexpr int KROW = D + 8;    // K tile row stride in LDS (halves), padded against bank conflicts
   constexpr int VROW = KT + 4;   // V^T tile row stride in LDS (halves)
-  constexpr int KCH = KT * CPR / 256;        // K chunks per thread
-  constexpr int VPR = (KT / 2) * CPR / 256;  // V key-pairs x chunks per thread
-  static_assert(KCH >= 1 && VPR >= 1, "tile too small for the workgroup");
+  constexpr int NKC = KT * CPR;          // K chunks per tile
+  constexpr int NVP = (KT / 2) * CPR;    // V (key pair, chunk) items per tile
+  constexpr int KCH = (NKC + 255) / 256;
+  constexpr int VPR = (NVP + 255) / 256;
 
-  __shared__ __align__(16) uint16_t sk[KT * KROW];
-  __shared__ __align__(16) uint16_t sv[D * VROW];
+  __shared__ __align__(16) uint16_t sk[2][KT * KROW];
+  __shared__ __align__(16) uint16_t sv[2][D * VROW];
+  __shared__ int32_t sbt[MAXB_LDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -106,6 +119,12 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
   const char* vc = reinterpret_cast<const char*>(a.v_cache);
   const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks;
 
+  // the blocks this workgroup reads, staged once
+  const int nb_needed = (kv_end + BS - 1) / BS;
+  const bool bt_in_lds = nb_needed <= MAXB_LDS;
+  if (bt_in_lds)
+    for (int i = tid; i < nb_needed; i += 256) sbt[i] = bt_row[i];
+
   // Q^T fragments (B operand of S^T = K Q^T): query n16 of group g, d = 32*ks + 8*g4 .. +7
   u32x4 qf[NQ][KS];
 #pragma unroll
@@ -132,6 +151,9 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
     for (int dt = 0; dt < NDT; ++dt) o[g][dt] = zero4();
   }
 
+  __syncthreads();  // block table visible
+  auto block_of = [&](int pos) -> int32_t { return bt_in_lds ? sbt[pos / BS] : bt_row[pos / BS]; };
+
   // ---- global -> registers for one tile (zeros past kv_end)
   u32x4 kreg[KCH], vreg[2 * VPR];
   auto fetch = [&](int t) {
@@ -142,10 +164,9 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
       const int key = ci / CPR, dc = ci % CPR;
       const int pos = kv0 + key;
       kreg[r] = u32x4{0u, 0u, 0u, 0u};
-      if (pos < kv_end) {
-        const int32_t phys = bt_row[pos / BS];
-        kreg[r] = *reinterpret_cast<const u32x4*>(kc + kv_row_offset(phys, h, pos % BS, a.H, BS, D) * 2 + dc * 16);
-      }
+      if (ci < NKC && pos < kv_end)
+        kreg[r] = *reinterpret_cast<const u32x4*>(kc + kv_row_offset(block_of(pos), h, pos % BS, a.H, BS, D) * 2 +
+                                                  dc * 16);
     }
 #pragma unroll
     for (int r = 0; r < VPR; ++r) {
@@ -155,125 +176,132 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
       for (int e = 0; e < 2; ++e) {
         const int pos = kv0 + 2 * kp + e;
         vreg[2 * r + e] = u32x4{0u, 0u, 0u, 0u};
-        if (pos < kv_end) {
-          const int32_t phys = bt_row[pos / BS];
-          vreg[2 * r + e] =
-              *reinterpret_cast<const u32x4*>(vc + kv_row_offset(phys, h, pos % BS, a.H, BS, D) * 2 + dc * 16);
-        }
+        if (pi < NVP && pos < kv_end)
+          vreg[2 * r + e] = *reinterpret_cast<const u32x4*>(
+              vc + kv_row_offset(block_of(pos), h, pos % BS, a.H, BS, D) * 2 + dc * 16);
       }
     }
   };
-  // ---- registers -> LDS: K row-major, V transposed (two keys packed per word)
-  auto stage = [&]() {
+  // ---- registers -> LDS buffer b: K row-major, V transposed (two keys packed per word)
+  auto stage = [&](int b) {
 #pragma unroll
     for (int r = 0; r < KCH; ++r) {
       const int ci = tid + 256 * r;
-      const int key = ci / CPR, dc = ci % CPR;
-      *reinterpret_cast<u32x4*>(&sk[key * KROW + dc * 8]) = kreg[r];
+      if (ci < NKC) {
+        const int key = ci / CPR, dc = ci % CPR;
+        *reinterpret_cast<u32x4*>(&sk[b][key * KROW + dc * 8]) = kreg[r];
+      }
     }
 #pragma unroll
     for (int r = 0; r < VPR; ++r) {
       const int pi = tid + 256 * r;
-      const int kp = pi / CPR, dc = pi % CPR;
-      const u32x4 v0 = vreg[2 * r], v1 = vreg[2 * r + 1];
+      if (pi < NVP) {
+        const int kp = pi / CPR, dc = pi % CPR;
+        const u32x4 v0 = vreg[2 * r], v1 = vreg[2 * r + 1];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t lo = (v0[w] & 0xffffu) | (v1[w] << 16);          // element 2w of keys 2kp, 2kp+1
-        const uint32_t hi = (v0[w] >> 16) | (v1[w] & 0xffff0000u);      // element 2w+1
-        *reinterpret_cast<uint32_t*>(&sv[(dc * 8 + 2 * w) * VROW + 2 * kp]) = lo;
-        *reinterpret_cast<uint32_t*>(&sv[(dc * 8 + 2 * w + 1) * VROW + 2 * kp]) = hi;
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t lo = (v0[w] & 0xffffu) | (v1[w] << 16);      // element 2w of keys 2kp, 2kp+1
+          const uint32_t hi = (v0[w] >> 16) | (v1[w] & 0xffff0000u);  // element 2w+1
+          *reinterpret_cast<uint32_t*>(&sv[b][(dc * 8 + 2 * w) * VROW + 2 * kp]) = lo;
+          *reinterpret_cast<uint32_t*>(&sv[b][(dc * 8 + 2 * w + 1) * VROW + 2 * kp]) = hi;
+        }
       }
     }
   };
 
-  fetch(0);
-  for (int t = 0; t < n_tiles; ++t) {
-    const int kv0 = t * KT;
-    __syncthreads();  // everyone is done reading the previous tile
-    stage();
-    __syncthreads();
-    if (t + 1 < n_tiles) fetch(t + 1);  // in flight during this tile's math
-
-    if (wave_active && kv0 <= wave_last_pos) {
-      // S^T = K Q^T for 4 key subtiles of 16
-      f32x4 sacc[NQ][4];
+  auto compute = [&](int b, int kv0) {
+    // S^T = K Q^T over NSUB key subtiles of 16
+    f32x4 sacc[NQ][NSUB];
 #pragma unroll
-      for (int g = 0; g < NQ; ++g)
+    for (int g = 0; g < NQ; ++g)
 #pragma unroll
-        for (int sub = 0; sub < 4; ++sub) sacc[g][sub] = zero4();
+      for (int sub = 0; sub < NSUB; ++sub) sacc[g][sub] = zero4();
 #pragma unroll
-      for (int sub = 0; sub < 4; ++sub) {
+    for (int sub = 0; sub < NSUB; ++sub) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const u32x4 ka = *reinterpret_cast<const u32x4*>(&sk[(sub * 16 + n16) * KROW + ks * 32 + 8 * g4]);
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 ka = *reinterpret_cast<const u32x4*>(&sk[b][(sub * 16 + n16) * KROW + ks * 32 + 8 * g4]);
 #pragma unroll
-          for (int g = 0; g < NQ; ++g) sacc[g][sub] = mfma<DT>(ka, qf[g][ks], sacc[g][sub]);
-        }
+        for (int g = 0; g < NQ; ++g) sacc[g][sub] = mfma<DT>(ka, qf[g][ks], sacc[g][sub]);
       }
-      // online softmax; lane holds query n16, keys kv0 + 16*sub + 4*g4 + i
-      u32x4 pb[NQ][2];
-      u32x4 pbl[NQ][2];  // bf16 remainders
+    }
+    // online softmax; lane holds query n16, keys kv0 + 16*sub + 4*g4 + i
+    u32x4 pb[NQ][NKST];
+    u32x4 pbl[NQ][NKST];  // bf16 remainders
 #pragma unroll
-      for (int g = 0; g < NQ; ++g) {
-        const int qpos = c0 + wq0 + g * 16 + n16;
-        const int last_key = min(qpos, kv_end - 1);
-        float sc[16];
-        float mt = -INFINITY;
+    for (int g = 0; g < NQ; ++g) {
+      const int qpos = c0 + wq0 + g * 16 + n16;
+      const int last_key = min(qpos, kv_end - 1);
+      float sc[4 * NSUB];
+      float mt = -INFINITY;
 #pragma unroll
-        for (int sub = 0; sub < 4; ++sub)
+      for (int sub = 0; sub < NSUB; ++sub)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = kv0 + 16 * sub + 4 * g4 + i;
-            const float x = sacc[g][sub][i] * a.scale_log2;
-            sc[4 * sub + i] = key <= last_key ? x : -INFINITY;
-            mt = fmaxf(mt, sc[4 * sub + i]);
-          }
-        mt = fmaxf(mt, shfl_xor_f(mt, 16));
-        mt = fmaxf(mt, shfl_xor_f(mt, 32));
-        const float m_new = fmaxf(m[g], mt);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m[g] - m_use);
-        float psum = 0.f;
-        uint32_t ph[16], pl[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(sc[i] - m_use);
-          psum += p;
-          ph[i] = to_bits<DT>(p);
-          pl[i] = DT == Dt::BF16 ? to_bits<DT>(p - from_bits<DT>(ph[i])) : 0u;
+        for (int i = 0; i < 4; ++i) {
+          const int key = kv0 + 16 * sub + 4 * g4 + i;
+          const float x = sacc[g][sub][i] * a.scale_log2;
+          sc[4 * sub + i] = key <= last_key ? x : -INFINITY;
+          mt = fmaxf(mt, sc[4 * sub + i]);
         }
-        l[g] = l[g] * alpha + psum;
-        m[g] = m_new;
+      mt = fmaxf(mt, shfl_xor_f(mt, 16));
+      mt = fmaxf(mt, shfl_xor_f(mt, 32));
+      const float m_new = fmaxf(m[g], mt);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m[g] - m_use);
+      float psum = 0.f;
+      uint32_t ph[4 * NSUB], pl[4 * NSUB];
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[g][dt] *= alpha;
-        // B operand of O^T += V^T P^T for key step kst: elements 0..3 from
-        // subtile 2*kst, 4..7 from subtile 2*kst+1
-#pragma unroll
-        for (int kst = 0; kst < 2; ++kst) {
-          const int b0 = 8 * kst;
-          pb[g][kst] = u32x4{ph[b0] | (ph[b0 + 1] << 16), ph[b0 + 2] | (ph[b0 + 3] << 16),
-                             ph[b0 + 4] | (ph[b0 + 5] << 16), ph[b0 + 6] | (ph[b0 + 7] << 16)};
-          pbl[g][kst] = u32x4{pl[b0] | (pl[b0 + 1] << 16), pl[b0 + 2] | (pl[b0 + 3] << 16),
-                              pl[b0 + 4] | (pl[b0 + 5] << 16), pl[b0 + 6] | (pl[b0 + 7] << 16)};
-        }
+      for (int i = 0; i < 4 * NSUB; ++i) {
+        const float p = __builtin_amdgcn_exp2f(sc[i] - m_use);
+        psum += p;
+        ph[i] = to_bits<DT>(p);
+        pl[i] = DT == Dt::BF16 ? to_bits<DT>(p - from_bits<DT>(ph[i])) : 0u;
       }
-      // O^T += V^T P^T: A = V^T rows d = 16*dt + n16, keys 32*kst + 4*g4 + {0..3} and +16
+      l[g] = l[g] * alpha + psum;
+      m[g] = m_new;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
+      for (int dt = 0; dt < NDT; ++dt) o[g][dt] *= alpha;
+      // B operand of O^T += V^T P^T for key step kst: elements 0..3 from
+      // subtile 2*kst, 4..7 from subtile 2*kst+1
 #pragma unroll
-        for (int kst = 0; kst < 2; ++kst) {
-          const uint16_t* row = &sv[(dt * 16 + n16) * VROW + kst * 32 + 4 * g4];
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(row);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 16);
-          const u32x4 va = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      for (int kst = 0; kst < NKST; ++kst) {
+        const int b0 = 8 * kst;
+        pb[g][kst] = u32x4{ph[b0] | (ph[b0 + 1] << 16), ph[b0 + 2] | (ph[b0 + 3] << 16),
+                           ph[b0 + 4] | (ph[b0 + 5] << 16), ph[b0 + 6] | (ph[b0 + 7] << 16)};
+        pbl[g][kst] = u32x4{pl[b0] | (pl[b0 + 1] << 16), pl[b0 + 2] | (pl[b0 + 3] << 16),
+                            pl[b0 + 4] | (pl[b0 + 5] << 16), pl[b0 + 6] | (pl[b0 + 7] << 16)};
+      }
+    }
+    // O^T += V^T P^T: A = V^T rows d = 16*dt + n16, keys 32*kst + 4*g4 + {0..3} and +16
 #pragma unroll
-          for (int g = 0; g < NQ; ++g) {
-            o[g][dt] = mfma<DT>(va, pb[g][kst], o[g][dt]);
-            if constexpr (DT == Dt::BF16) o[g][dt] = mfma<DT>(va, pbl[g][kst], o[g][dt]);
-          }
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+      for (int kst = 0; kst < NKST; ++kst) {
+        const uint16_t* row = &sv[b][(dt * 16 + n16) * VROW + kst * 32 + 4 * g4];
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(row);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 16);
+        const u32x4 va = u32x4{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+        for (int g = 0; g < NQ; ++g) {
+          o[g][dt] = mfma<DT>(va, pb[g][kst], o[g][dt]);
+          if constexpr (DT == Dt::BF16) o[g][dt] = mfma<DT>(va, pbl[g][kst], o[g][dt]);
         }
       }
     }
+  };
+
+  // Double-buffered LDS: tile t+1 travels global -> registers while tile t
+  // is computed, then lands in the other buffer; one barrier per tile.
+  fetch(0);
+  stage(0);
+  __syncthreads();
+  for (int t = 0; t < n_tiles; ++t) {
+    const bool more = t + 1 < n_tiles;
+    if (more) fetch(t + 1);
+    const int kv0 = t * KT;
+    if (wave_active && kv0 <= wave_last_pos) compute(t & 1, kv0);
+    if (more) stage((t + 1) & 1);
+    __syncthreads();
   }
 
   if (!wave_active) return;

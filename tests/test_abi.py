@@ -88,8 +88,9 @@ def test_decode_validation(fn):
     P = pa.decode_partition_tokens()
     need = pa.decode_workspace_bytes(4, 2, 128, 2 * P)
     assert need == 4 * 2 * 2 * (128 + 2) * 4
-    assert _dec(fn, maxb=64, maxctx=2 * P, ws=FAKE, wsb=need - 4) == pa.PA_ERR_WORKSPACE
-    assert _dec(fn, maxb=64, maxctx=2 * P, ws=ctypes.c_void_p(0x1004), wsb=need) == pa.PA_ERR_WORKSPACE
+    maxb = 2 * P // 16
+    assert _dec(fn, maxb=maxb, maxctx=2 * P, ws=FAKE, wsb=need - 4) == pa.PA_ERR_WORKSPACE
+    assert _dec(fn, maxb=maxb, maxctx=2 * P, ws=ctypes.c_void_p(0x1004), wsb=need) == pa.PA_ERR_WORKSPACE
 
 
 def test_workspace_size_rules():

@@ -232,3 +232,51 @@ def test_prefill_single_query_chunk_matches_decode():
     pa.paged_attention_decode(out, od.pf_q, od.k_cache, od.v_cache, od.pf_block_tables, od.pf_context_lens,
                               wl.scale, max_context_len=p.max_context_len)
     assert np.abs(pf - host(out).astype(np.float64)).max() <= 2 * ATOL["f16"]
+
+
+# ------------------------------------------------------------- HIP graphs
+
+def _capture(fn):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def test_mixed_step_graph_replays_match_eager():
+    """The whole mixed step (cache write, prefill, split-K decode) captured as
+    a HIP graph: every replay, with eager work and syncs in between, equals the
+    eager step bit for bit."""
+    wl, _, _ = _config(5)
+    od = OnDevice(wl)
+    d, p = wl.decode, wl.prefill
+    ws = pa.make_decode_workspace(d.num_seqs, wl.num_heads, wl.head_dim, d.max_context_len)
+    dout = torch.empty_like(od.q)
+    pout = torch.empty_like(od.pf_q)
+
+    def step():
+        pa.reshape_and_cache(od.new_k, od.new_v, od.k_cache, od.v_cache, od.slot_mapping)
+        pa.paged_attention_prefill(pout, od.pf_q, od.k_cache, od.v_cache, od.pf_block_tables, od.pf_context_lens,
+                                   od.pf_qsl, wl.scale, p.max_q_len, p.max_context_len)
+        pa.paged_attention_decode(dout, od.q, od.k_cache, od.v_cache, od.block_tables, od.context_lens, wl.scale,
+                                  d.max_context_len, ws)
+
+    step()
+    torch.cuda.synchronize()
+    dref, pref = dout.clone(), pout.clone()
+    g = _capture(step)
+    for i in range(4):
+        dout.zero_()
+        pout.zero_()
+        extra = od.decode(torch.float32)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dout, dref), f"decode differs on replay {i}"
+        assert torch.equal(pout, pref), f"prefill differs on replay {i}"
+        assert torch.isfinite(extra).all()
