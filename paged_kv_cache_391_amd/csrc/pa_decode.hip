@@ -24,7 +24,10 @@
 //   * the block-table entries of a wave's tiles are fetched with one vector
 //     load and read out with readlane, so the dependent table load is paid
 //     once per 64 tiles, and the next tile's K and V are in flight while the
-//     current one is consumed.
+//     current one is consumed;
+//   * K and V are read with non-temporal loads: every cached byte is used
+//     once per step, and the streaming hint lifts the measured read rate of
+//     random 4 KiB tiles from ~5.9 to ~6.6 TB/s on gfx950.
 // Long contexts are cut into partitions of kPartitionTokens tokens (whole
 // blocks). A sequence with one partition is finished in place; otherwise
 // each partition writes (m, l, acc[D]) and K3 merges them with log-sum-exp
@@ -59,15 +62,18 @@ template <Dt DT, int D> struct Lane {
   // the scalar-base + vector-offset form and every tile's address is formed
   // with scalar arithmetic only. Load j of the lane covers 16*VB contiguous
   // bytes together with the other 15 lanes of its row.
+  template <bool NT = false>
   __device__ static __forceinline__ void load(uint32_t (&w)[WPL], const char* base, uint32_t lane_off) {
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       if constexpr (VB == 16) {
-        const uint4 x = *reinterpret_cast<const uint4*>(base + lane_off + j * 16 * VB);
-        w[j * 4 + 0] = x.x; w[j * 4 + 1] = x.y; w[j * 4 + 2] = x.z; w[j * 4 + 3] = x.w;
+        const u32x4 x = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + lane_off + j * 16 * VB))
+                           : *reinterpret_cast<const u32x4*>(base + lane_off + j * 16 * VB);
+        w[j * 4 + 0] = x[0]; w[j * 4 + 1] = x[1]; w[j * 4 + 2] = x[2]; w[j * 4 + 3] = x[3];
       } else {
-        const uint2 x = *reinterpret_cast<const uint2*>(base + lane_off + j * 16 * VB);
-        w[j * 2 + 0] = x.x; w[j * 2 + 1] = x.y;
+        const u32x2 x = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base + lane_off + j * 16 * VB))
+                           : *reinterpret_cast<const u32x2*>(base + lane_off + j * 16 * VB);
+        w[j * 2 + 0] = x[0]; w[j * 2 + 1] = x[1];
       }
     }
   }
@@ -179,7 +185,7 @@ __device__ __forceinline__ void prefill_row(const int32_t* qsl, const int32_t* c
 }  // namespace
 
 template <Dt DT, int D, int BS, int HG, bool PF>
-__global__ __launch_bounds__(HG * 64) void decode_partition_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(HG * 64, PA_DECODE_MIN_WAVES) void decode_partition_kernel(const DecodeArgs a) {
   using L = Lane<DT, D>;
   constexpr int WPL = L::WPL;
   constexpr int TPB = BS / 16;  // tiles per block
@@ -243,27 +249,34 @@ __global__ __launch_bounds__(HG * 64) void decode_partition_kernel(const DecodeA
     };
     auto load_tile = [&](uint32_t (&kw)[4][WPL], uint32_t (&vw)[4][WPL], int64_t off) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) L::load(kw[j], kc + off + j * 4 * L::ROW_BYTES, lane_off);
+      for (int j = 0; j < 4; ++j) L::template load<true>(kw[j], kc + off + j * 4 * L::ROW_BYTES, lane_off);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) L::load(vw[j], vc + off + j * 4 * L::ROW_BYTES, lane_off);
+      for (int j = 0; j < 4; ++j) L::template load<true>(vw[j], vc + off + j * 4 * L::ROW_BYTES, lane_off);
       // keep the loads issued here, ahead of the other buffer's math
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    // Two register buffers, next tile always in flight. The loop body has no
-    // branch (past the end it re-reads the last tile, a cache hit) so the
-    // compiler's wait counts stay exact and never drain the load queue.
+    // Two register buffers, next tile always in flight. The steady-state
+    // loop body has no branch, so the compiler's wait counts stay exact and
+    // never drain the load queue; the last one or two tiles are finished
+    // after it, so every tile is fetched exactly once.
     uint32_t ka[4][WPL], va[4][WPL], kb[4][WPL], vb[4][WPL];
     int ta, tb0;
     load_tile(ka, va, tile_off(0, ta));
     int i = 0;
-    for (; i + 1 < cnt; i += 2) {
+    for (; i + 2 < cnt; i += 2) {
       load_tile(kb, vb, tile_off(i + 1, tb0));
       consume_tile<DT, D>(st, qw, ka, va, ta, ctx, g, a.scale_log2);
-      load_tile(ka, va, tile_off(min(i + 2, cnt - 1), ta));
+      load_tile(ka, va, tile_off(i + 2, ta));
       consume_tile<DT, D>(st, qw, kb, vb, tb0, ctx, g, a.scale_log2);
     }
-    if (i < cnt) consume_tile<DT, D>(st, qw, ka, va, ta, ctx, g, a.scale_log2);
+    if (i + 1 < cnt) {
+      load_tile(kb, vb, tile_off(i + 1, tb0));
+      consume_tile<DT, D>(st, qw, ka, va, ta, ctx, g, a.scale_log2);
+      consume_tile<DT, D>(st, qw, kb, vb, tb0, ctx, g, a.scale_log2);
+    } else {
+      consume_tile<DT, D>(st, qw, ka, va, ta, ctx, g, a.scale_log2);
+    }
   }
 
   // merge the four 16-lane rows of the wave (same lane column c)

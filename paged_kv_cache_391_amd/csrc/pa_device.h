@@ -12,6 +12,8 @@ namespace pa {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 enum class Dt : int { F32 = 0, F16 = 1, BF16 = 2 };
 

@@ -7,10 +7,14 @@
 
 #include "pa_device.h"
 
-// Decode tuning: heads per workgroup (one wave each) and tokens per split-K
-// partition.
+// Decode tuning: heads per workgroup (one wave each), the number of waves
+// per SIMD the partition kernel's register budget must leave room for, and
+// tokens per split-K partition.
 #ifndef PA_DECODE_HEADS
-#define PA_DECODE_HEADS 1
+#define PA_DECODE_HEADS 2
+#endif
+#ifndef PA_DECODE_MIN_WAVES
+#define PA_DECODE_MIN_WAVES 5
 #endif
 #ifndef PA_PARTITION_TOKENS
 #define PA_PARTITION_TOKENS 512
