@@ -1,20 +1,31 @@
 #!/usr/bin/env python3
-"""Paged decode attention throughput at the LLaMA-7B layer shape on one MI355X.
+"""Paged attention throughput on one MI355X, against the HBM and MFMA rooflines.
 
-Workload (seeded, synthetic): 64 sequences x 32 heads x head_dim 128, f16,
-block_size 16, context lengths ~ U[128, 2048], block tables = slices of one
-random permutation of a pool sized to fit exactly, q/K/V ~ N(0,1).
+Default workload (seeded, synthetic): one decode iteration of one LLaMA-7B
+attention layer -- 64 sequences x 32 heads x head_dim 128, f16, block_size
+16, context lengths ~ U[128, 2048], block tables = slices of one random
+permutation of a pool sized to fit exactly, q/K/V ~ N(0,1).
 
-One step = one decode iteration of one attention layer, all inputs resident
-in HBM: reshape_and_cache of the 64 new tokens, then split-K decode
-(partition kernel + reduction kernel) with an f16 output. The timed steps
-replay the step captured as a HIP graph (checked bit-identical to the eager
-step); --eager times plain launches instead.
+Other workloads (``--workload``), same machinery:
+  mixed256    256 sequences x 32 x 128, bf16, block_size 32, lognormal
+              context lengths (mean ~600, clipped to [1, 4096]), 1.25x pool
+  prefix13b   32 prompts x 8 samples, 40 x 128, f16, block_size 16, a
+              1024-token prompt whose blocks all 8 samples share, tails U[0,256]
+  mixed_step  40 x 128, f16, block_size 16: cache write of 2048 rows, causal
+              prefill of 4 chunks (L ~ U[256,512] after U[0,1024] cached
+              tokens) and decode of 96 sequences (ctx ~ U[256,4096])
+
+One step = the workload's whole path, all inputs resident in HBM:
+reshape_and_cache of the step's new tokens, [prefill,] then split-K decode
+(partition kernel + reduction kernel) with an output in the input dtype.
+The timed steps replay the step captured as a HIP graph (checked
+bit-identical to the eager step); --eager times plain launches instead.
 
 Prints ONE JSON line: value = algorithmic bytes of the step / step time
-(GB/s, 1e9 B/s); roofline = the partition kernel's algorithmic bytes over its
-average launch time (HIP events on the launch stream) against the 8 TB/s HBM
-peak; cpu_baseline = the fp64 oracle on the host cores over the same decode.
+(GB/s, 1e9 B/s); roofline = the decode partition kernel's algorithmic bytes
+over its average launch time (HIP events on the launch stream) against the
+8 TB/s HBM peak; cpu_baseline = the fp64 oracle on the host cores over the
+same work.
 """
 import argparse
 import hashlib
@@ -28,9 +39,27 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention achieved HBM GB/s (% of peak) at LLaMA-7B layer shape"
+METRIC_OTHER = "paged attention step achieved HBM GB/s (% of peak)"
 HBM_PEAK_GBPS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama7b_traffic.json")
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # dense fp16/bf16 matrix-core peak of MI355X
 KERNEL_SOURCES = ["pa_decode.hip", "pa_device.h", "pa_internal.h"]
+CPU_SECONDS = 10.0  # the oracle repeats its pass until about this much CPU time has elapsed
+
+WORKLOADS = {
+    "llama7b": "llama7b_decode_step: reshape_and_cache of 64 new tokens + split-K paged decode, 64 seqs x 32 heads "
+               "x 128, f16, block_size 16, ctx U[128,2048], seed 393",
+    "mixed256": "mixed256_decode_step: reshape_and_cache of 256 new tokens + split-K paged decode, 256 seqs x 32 "
+                "heads x 128, bf16, block_size 32, ctx lognormal(mean 600) clipped to [1,4096], 1.25x pool, seed 394",
+    "prefix13b": "prefix13b_decode_step: 32 prompts x 8 samples sharing a 1024-token prompt's blocks, tails "
+                 "U[0,256], 40 heads x 128, f16, block_size 16, seed 395",
+    "mixed_step": "mixed_step: reshape_and_cache of 2048 rows + causal prefill of 4 chunks (L U[256,512], prior "
+                  "U[0,1024]) + split-K decode of 96 seqs (ctx U[256,4096]), 40 heads x 128, f16, block_size 16, "
+                  "seed 396",
+}
+
+
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
 
 
 def kernel_source_hash():
@@ -60,7 +89,7 @@ def _counter_rows(path):
     return rows
 
 
-def record_traffic(fetch_dir, write_dir, copy_bytes):
+def record_traffic(workload, fetch_dir, write_dir, copy_bytes):
     """Turn two counter runs of this benchmark (FETCH_SIZE, then WRITE_SIZE;
     both in KiB per dispatch) into HBM bytes per launch of the partition
     kernel, each scaled by what the same counter reads for the plain device
@@ -71,27 +100,106 @@ def record_traffic(fetch_dir, write_dir, copy_bytes):
         rows = _counter_rows(d)
         part = [v for k, v in rows if "decode_partition_kernel" in k]
         copy = [v for k, v in rows if "copyBuffer" in k or "copy" in k.lower()]
-        copy = max(copy)  # the 1 GiB probe copy is the largest copy dispatch
+        copy = max(copy)  # the probe copy is the largest copy dispatch
         scale = (copy_bytes / 1024.0) / copy
         out[name] = {"partition_kernel_kib_avg": sum(part) / len(part), "copy_kib": copy, "scale": scale,
                      "dispatches": len(part)}
     fetch = out["fetch"]["partition_kernel_kib_avg"] * 1024 * out["fetch"]["scale"]
     write = out["write"]["partition_kernel_kib_avg"] * 1024 * out["write"]["scale"]
-    rec = {"kernel": "decode_partition_kernel<f16,128,16>", "workload": "llama7b decode (bench.py)",
+    rec = {"kernel": "decode_partition_kernel", "workload": f"{workload} (bench.py --workload {workload})",
            "kernel_source_sha256": kernel_source_hash(), "hbm_bytes_per_launch": round(fetch + write),
            "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write), "counters": out}
     import paged_kv_cache_391_amd as pa
     rec["partition_tokens"] = pa.decode_partition_tokens()
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(traffic_file(workload), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec, indent=1))
 
 
+def decode_bytes(ctx, H, D, elt, bs):
+    """Algorithmic bytes of decode over valid tokens: K and V of every valid
+    token, one table entry per used block, the context length, q and out."""
+    import numpy as np
+    ctx = ctx.astype(np.int64)
+    S = ctx.shape[0]
+    kv = int(ctx.sum()) * H * D * elt * 2
+    table = int(np.ceil(ctx / bs).sum()) * 4 + 4 * S
+    return kv, table, 2 * S * H * D * elt
+
+
+def partition_kernel_bytes(ctx, H, D, elt, bs, P):
+    """Bytes the partition kernel must move: K/V, table entries and q, plus
+    either the final output row or (m, l, acc) per partition."""
+    import numpy as np
+    ctx = ctx.astype(np.int64)
+    kv, table, _ = decode_bytes(ctx, H, D, elt, bs)
+    S = ctx.shape[0]
+    nparts = np.ceil(np.ceil(ctx / 16) / (P // 16)).astype(np.int64)
+    writes = int(np.where(nparts > 1, nparts * H * (D + 2) * 4, H * D * elt).sum())
+    return kv + table + S * H * D * elt + writes
+
+
+def unique_kv_bytes(block_tables, ctx, H, D, elt, bs):
+    """K/V bytes of the distinct cache slots the step reads (aliased blocks
+    counted once)."""
+    import numpy as np
+    slots = []
+    for s in range(ctx.shape[0]):
+        t = np.arange(int(ctx[s]))
+        slots.append(block_tables[s, t // bs].astype(np.int64) * bs + t % bs)
+    n = np.unique(np.concatenate(slots)).size if slots else 0
+    return int(n) * H * D * elt * 2
+
+
+def prefill_work(p, H, D, elt):
+    """(flops, bytes) of causal prefill: unmasked query-key pairs only; each
+    chunk reads its context's K/V once and its q, writes its out."""
+    import numpy as np
+    L = np.diff(p.query_start_loc).astype(np.int64)
+    ctx = p.context_lens.astype(np.int64)
+    c = ctx - L
+    flops = int((4 * D * H * (L * c + L * (L + 1) // 2)).sum())
+    byts = int((ctx * H * D * elt * 2 + 2 * L * H * D * elt).sum())
+    return flops, byts
+
+
+def cpu_baseline(wl, threads):
+    """The fp64 oracle, as it stands, over the same decode (and prefill)
+    work, repeated until about CPU_SECONDS have elapsed."""
+    import oracle
+    kc, vc = oracle.reshape_and_cache(wl.new.k, wl.new.v, wl.k_cache, wl.v_cache, wl.new.slot_mapping,
+                                      wl.block_size, wl.dtype)
+    d, p = wl.decode, wl.prefill
+    H, D, elt, bs = wl.num_heads, wl.head_dim, wl.elt_bytes, wl.block_size
+
+    def one_pass():
+        if p is not None:
+            oracle.prefill(p.q, kc, vc, p.block_tables, p.context_lens, p.query_start_loc, wl.scale, wl.dtype,
+                           threads=threads)
+        oracle.decode(d.q, kc, vc, d.block_tables, d.context_lens, wl.scale, wl.dtype, threads=threads)
+
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        one_pass()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= CPU_SECONDS or reps >= 1000:
+            break
+    per = el / reps
+    kv, table, qo = decode_bytes(d.context_lens, H, D, elt, bs)
+    byts = kv + table + qo + (prefill_work(p, H, D, elt)[1] if p is not None else 0)
+    what = "prefill of the 4 chunks + decode" if p is not None else "the whole decode"
+    return {"value": round(byts / per / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{what} of this workload, {reps} pass(es) in {el:.1f} s ({per:.3f} s each); fp64, gather + "
+                      "softmax attention per (row, head), OpenMP over pairs; same algorithmic-byte count as value"}
+
+
 def main():
-    ap = argparse.ArgumentParser(description=__doc__)
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", choices=list(WORKLOADS), default="llama7b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--copy-probe-gib", type=float, default=1.0, help="size of the plain-copy bandwidth probe")
@@ -99,7 +207,8 @@ def main():
                     help="store HBM bytes per launch from two rocprofv3 --pmc runs of this script and exit")
     args = ap.parse_args()
     if args.record_traffic:
-        record_traffic(args.record_traffic[0], args.record_traffic[1], int(args.copy_probe_gib * (1 << 30)))
+        record_traffic(args.workload, args.record_traffic[0], args.record_traffic[1],
+                       int(args.copy_probe_gib * (1 << 30)))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         log("bench.py measures one GPU only: each GPU would run this path on its own share of sequences or "
@@ -111,64 +220,73 @@ def main():
 
     import paged_kv_cache_391_amd as pa
     from tests._gpu import OnDevice
-    from workloads import config2
+    from workloads import config2, config3, config4, config5
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     t = time.time()
-    wl = config2()
-    log(f"[bench] generated workload in {time.time() - t:.1f}s: {wl.num_blocks} blocks, "
+    wl = {"llama7b": config2, "mixed256": config3, "prefix13b": config4, "mixed_step": config5}[args.workload]()
+    log(f"[bench] {args.workload}: generated in {time.time() - t:.1f}s: {wl.num_blocks} blocks, "
         f"sum ctx {int(wl.decode.context_lens.sum())}")
     od = OnDevice(wl)
-    d = wl.decode
+    d, p = wl.decode, wl.prefill
     S, H, D, bs, elt = d.num_seqs, wl.num_heads, wl.head_dim, wl.block_size, wl.elt_bytes
     maxctx = d.max_context_len
     ws = pa.make_decode_workspace(S, H, D, maxctx)
-    out = torch.empty_like(od.q)  # f16 output: the production path
+    out = torch.empty_like(od.q)  # output in the input dtype: the production path
+    pf_out = torch.empty_like(od.pf_q) if p is not None else None
     P = pa.decode_partition_tokens()
 
     def step(ev=None):
-        pa.reshape_and_cache(od.new_k, od.new_v, od.k_cache, od.v_cache, od.slot_mapping)
         if ev is not None:
             ev[0].record()
+        pa.reshape_and_cache(od.new_k, od.new_v, od.k_cache, od.v_cache, od.slot_mapping)
+        if ev is not None:
+            ev[1].record()
+        if p is not None:
+            pa.paged_attention_prefill(pf_out, od.pf_q, od.k_cache, od.v_cache, od.pf_block_tables,
+                                       od.pf_context_lens, od.pf_qsl, wl.scale, max_q_len=p.max_q_len,
+                                       max_context_len=p.max_context_len)
+        if ev is not None:
+            ev[2].record()
         pa.paged_attention_decode_partitions(out, od.q, od.k_cache, od.v_cache, od.block_tables, od.context_lens,
                                              wl.scale, maxctx, ws)
         if ev is not None:
-            ev[1].record()
+            ev[3].record()
         pa.paged_attention_decode_reduce(out, od.context_lens, D, maxctx, od.q.dtype, ws)
         if ev is not None:
-            ev[2].record()
+            ev[4].record()
 
-    # ---- algorithmic bytes (valid tokens only)
-    ctx = d.context_lens.astype(np.int64)
-    kv_bytes = int(ctx.sum()) * H * D * elt * 2
-    table_bytes = int(np.ceil(ctx / bs).sum()) * 4 + 4 * S
-    qo_bytes = 2 * S * H * D * elt
+    # ---- algorithmic work (valid tokens only)
+    kv, table, qo = decode_bytes(d.context_lens, H, D, elt, bs)
     T = int(wl.new.slot_mapping.shape[0])
-    cache_write_bytes = 4 * T * H * D * elt + 4 * T
-    nparts = np.ceil(np.ceil(ctx / 16) / (P // 16)).astype(np.int64)
-    k2_writes = int(np.where(nparts > 1, nparts * H * (D + 2) * 4, H * D * elt).sum())
-    k2_bytes = kv_bytes + table_bytes + S * H * D * elt + k2_writes
-    decode_bytes = kv_bytes + table_bytes + qo_bytes
-    step_bytes = decode_bytes + cache_write_bytes
+    t_valid = int((wl.new.slot_mapping >= 0).sum())
+    cache_write_bytes = 4 * t_valid * H * D * elt + 4 * T
+    k2_bytes = partition_kernel_bytes(d.context_lens, H, D, elt, bs, P)
+    pf_flops, pf_bytes = prefill_work(p, H, D, elt) if p is not None else (0, 0)
+    step_bytes = kv + table + qo + cache_write_bytes + pf_bytes
 
-    # eager pass: HIP events on the launch stream around every partition-kernel launch
+    # eager pass: HIP events on the launch stream around every kernel launch
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    k2_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    k3_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+
+    def phase_ms(a, b):
+        return sum(e[a].elapsed_time(e[b]) for e in evs) / args.steps
+
+    cw_ms, pf_ms, k2_ms, k3_ms = phase_ms(0, 1), phase_ms(1, 2), phase_ms(2, 3), phase_ms(3, 4)
     eager_out = out.clone()
+    eager_pf = pf_out.clone() if pf_out is not None else None
 
     # timed pass: the step captured once as a HIP graph and replayed, as a
-    # serving loop runs decode (no host launch gaps between the 3 kernels)
+    # serving loop runs it (no host launch gaps between the kernels)
     ms_per_step = eager_ms
     graph_ok = None
     if not args.eager:
@@ -180,24 +298,33 @@ def main():
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             step()
+
+        def same():
+            ok = bool(torch.equal(out, eager_out))
+            return ok and (pf_out is None or bool(torch.equal(pf_out, eager_pf)))
+
         graph_ok = True
         for _ in range(max(1, args.warmup)):
             out.zero_()
+            if pf_out is not None:
+                pf_out.zero_()
             graph.replay()
             torch.cuda.synchronize()
-            graph_ok = graph_ok and bool(torch.equal(out, eager_out))
+            graph_ok = graph_ok and same()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(args.steps):
             graph.replay()
         torch.cuda.synchronize()
         ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
-        graph_ok = graph_ok and bool(torch.equal(out, eager_out))
+        graph_ok = graph_ok and same()
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     k2_gbps = k2_bytes / (k2_ms * 1e-3) / 1e9
     log(f"[bench] {ms_per_step * 1e3:.1f} us/step ({'graph' if not args.eager else 'eager'}; eager "
-        f"{eager_ms * 1e3:.1f} us), partition kernel {k2_ms * 1e3:.1f} us ({k2_gbps:.0f} GB/s), "
-        f"reduction {k3_ms * 1e3:.1f} us, graph output == eager: {graph_ok}")
+        f"{eager_ms * 1e3:.1f} us): cache write {cw_ms * 1e3:.1f} us"
+        + (f", prefill {pf_ms * 1e3:.1f} us ({pf_flops / (pf_ms * 1e-3) / 1e12:.0f} TFLOP/s)" if p else "")
+        + f", partition kernel {k2_ms * 1e3:.1f} us ({k2_gbps:.0f} GB/s), reduction {k3_ms * 1e3:.1f} us, "
+          f"graph output == eager: {graph_ok}")
     if graph_ok is False:
         raise SystemExit("graph replay disagrees with the eager step")
 
@@ -218,26 +345,18 @@ def main():
     del src, dst
 
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        rec = json.load(open(TRAFFIC_FILE))
+    tf = traffic_file(args.workload)
+    if os.path.exists(tf):
+        rec = json.load(open(tf))
         if rec.get("kernel_source_sha256") == kernel_source_hash() and rec.get("partition_tokens") == P:
             traffic = rec.get("hbm_bytes_per_launch")
 
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        kc, vc = oracle.reshape_and_cache(wl.new.k, wl.new.v, wl.k_cache, wl.v_cache, wl.new.slot_mapping, bs,
-                                          wl.dtype)
-        threads = max(1, min(16, os.cpu_count() or 1))
-        t = time.perf_counter()
-        oracle.decode(d.q, kc, vc, d.block_tables, d.context_lens, wl.scale, wl.dtype, threads=threads)
-        cpu_s = time.perf_counter() - t
-        cpu = {"value": round(decode_bytes / cpu_s / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-               "sample": f"the whole decode of this workload ({S} seqs x {H} heads, one pass, {cpu_s:.2f} s); "
-                         "fp64, gather + softmax attention per (seq, head), OpenMP over pairs"}
+        cpu = cpu_baseline(wl, max(1, min(16, os.cpu_count() or 1)))
 
     rec = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload == "llama7b" else METRIC_OTHER,
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -247,23 +366,37 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {"workload": "llama7b_decode_step: reshape_and_cache of 64 new tokens + split-K paged decode, "
-                               "64 seqs x 32 heads x 128, f16, block_size 16, ctx U[128,2048], seed 393",
-                   "global_batch": S, "seq_len": int(maxctx), "partition_tokens": P, "parallelism": "none (1 GPU)"},
+        "config": {"workload": WORKLOADS[args.workload], "global_batch": S, "seq_len": int(maxctx),
+                   "partition_tokens": P, "parallelism": "none (1 GPU)"},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(k2_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(k2_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": "decode_partition_kernel<f16,128,16>", "bytes_per_launch": k2_bytes,
+                     "kernel": f"decode_partition_kernel<{wl.dtype},{D},{bs}>", "bytes_per_launch": k2_bytes,
                      "avg_launch_us": round(k2_ms * 1e3, 2)},
         "timing": "hip_graph_replay" if not args.eager else "eager",
         "eager_ms_per_step": round(eager_ms, 5),
         "hbm_copy_probe_GBps": round(copy_gbps, 1),
         "step_bytes": step_bytes,
-        "reduce_kernel_avg_us": round(k3_ms * 1e3, 2),
+        "phases_us": {"reshape_and_cache": round(cw_ms * 1e3, 2), "decode_partitions": round(k2_ms * 1e3, 2),
+                      "decode_reduce": round(k3_ms * 1e3, 2)},
         "cpu_baseline": cpu,
     }
+    if args.workload == "prefix13b":
+        uniq = unique_kv_bytes(d.block_tables, d.context_lens, H, D, elt, bs)
+        rec["aliasing"] = {"logical_kv_bytes": kv, "unique_kv_bytes": uniq,
+                           "logical_GBps": round(kv / (k2_ms * 1e-3) / 1e9, 1),
+                           "unique_GBps": round(uniq / (k2_ms * 1e-3) / 1e9, 1)}
+    if p is not None:
+        pf_tflops = pf_flops / (pf_ms * 1e-3) / 1e12
+        rec["phases_us"]["prefill"] = round(pf_ms * 1e3, 2)
+        rec["prefill"] = {"bound": "mfma", "flops": pf_flops, "achieved_TFLOPs": round(pf_tflops, 1),
+                          "peak_TFLOPs": MFMA_PEAK_TFLOPS[wl.dtype],
+                          "mfma_frac": round(pf_tflops / MFMA_PEAK_TFLOPS[wl.dtype], 4), "bytes": pf_bytes,
+                          "hbm_frac": round(pf_bytes / (pf_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                          "roofline_us": round(max(pf_flops / (MFMA_PEAK_TFLOPS[wl.dtype] * 1e12),
+                                                   pf_bytes / (HBM_PEAK_GBPS * 1e9)) * 1e6, 2)}
     print(json.dumps(rec), flush=True)
 
 
