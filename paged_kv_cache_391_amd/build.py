@@ -15,6 +15,10 @@ def hipcc_flags(extra=()):
         "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
         # no packed-fp32 VALU ops: keep every fp32 op scalar per lane
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # matrix-core accumulators in ordinary VGPRs: the online softmax
+        # rescales them every tile, which would otherwise copy them out of
+        # and back into the accumulation registers
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-Wall", "-Wno-unused-function",
         *extra,
     ]

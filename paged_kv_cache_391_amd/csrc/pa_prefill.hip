@@ -14,15 +14,18 @@
 // is exactly the B operand P^T needs, so P never leaves registers; the
 // price is a transposed V tile, which the workgroup writes into LDS while
 // staging it. Per tile of KT keys (32 or 64):
-//   * the workgroup stages the sequence's block-table row in LDS once, then
-//     256 threads gather each K tile (row-major) and V tile (transposed)
-//     through it into one of two LDS buffers; the next tile's global loads
-//     are in flight while the current tile is computed, one barrier per tile;
+//   * the workgroup keeps a window of the sequence's block-table row in
+//     LDS; 256 threads gather each K tile (row-major) and V tile
+//     (transposed) through it into one of two LDS buffers. Tile t+2's
+//     global loads are in flight while tile t is computed and tile t+1 is
+//     staged, one barrier per tile;
 //   * each wave owns NQ groups of 16 queries; every K or V^T fragment read
 //     from LDS feeds one MFMA per group;
 //   * online softmax per query: in-lane max/sum over the lane's keys plus
-//     two cross-row shuffles; tiles past a wave's last query are skipped and
-//     only the diagonal tiles carry a mask.
+//     two cross-row shuffles; only tiles that cross a wave's first query
+//     carry the causal mask, tiles past its last query are skipped, and the
+//     running max is raised lazily (see compute()) so the accumulators are
+//     rescaled only on the few tiles that need it.
 // P is rounded to the input type for the P.V product; for bf16 it is split
 // into a bf16 head and a bf16 remainder (two MFMAs) to keep ~16 bits.
 #include "pa_internal.h"
@@ -39,13 +42,14 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 #define PA_PREFILL_KT 32
 #endif
 #ifndef PA_PREFILL_NQ
-#define PA_PREFILL_NQ 1
+#define PA_PREFILL_NQ 2
 #endif
 constexpr int KT = PA_PREFILL_KT;  // keys per tile (32 or 64)
 constexpr int NQ = PA_PREFILL_NQ;  // 16-query groups per wave
 constexpr int QW = 16 * NQ;        // queries per wave
 constexpr int QT = 4 * QW;         // queries per workgroup
-constexpr int MAXB_LDS = 512;      // block-table entries staged in LDS
+constexpr int MAXB_LDS = 256;      // block-table entries staged in LDS (a sliding window)
+constexpr float RESCALE_LOG2 = 8.f; // lazy rescale threshold (log2 units): p < 256 between rescales
 static_assert(KT == 32 || KT == 64, "key tile must be 32 or 64");
 
 template <Dt DT> __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
@@ -117,11 +121,11 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
   const char* vc = reinterpret_cast<const char*>(a.v_cache);
   const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks;
 
-  // the blocks this workgroup reads, staged once
+  // the table entries this workgroup reads sit in LDS: a window of
+  // MAXB_LDS entries starting at w0, moved forward when a tile leaves it
   const int nb_needed = (kv_end + BS - 1) / BS;
-  const bool bt_in_lds = nb_needed <= MAXB_LDS;
-  if (bt_in_lds)
-    for (int i = tid; i < nb_needed; i += 256) sbt[i] = bt_row[i];
+  int w0 = 0;
+  for (int i = tid; i < min(nb_needed, MAXB_LDS); i += 256) sbt[i] = bt_row[i];
 
   // Q^T fragments (B operand of S^T = K Q^T): query n16 of group g, d = 32*ks + 8*g4 .. +7
   u32x4 qf[NQ][KS];
@@ -150,52 +154,66 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
   }
 
   __syncthreads();  // block table visible
-  auto block_of = [&](int pos) -> int32_t { return bt_in_lds ? sbt[pos / BS] : bt_row[pos / BS]; };
+  auto block_of = [&](int pos) -> int32_t { return sbt[pos / BS - w0]; };
+  // make the window cover tile t (uniform across the workgroup; called where
+  // no thread is reading the window)
+  auto window_for = [&](int t) {
+    const int last = (min((t + 1) * KT, kv_end) - 1) / BS;
+    if (last >= w0 + MAXB_LDS) {
+      __syncthreads();
+      w0 = (t * KT) / BS;
+      for (int i = tid; i < min(nb_needed - w0, MAXB_LDS); i += 256) sbt[i] = bt_row[w0 + i];
+      __syncthreads();
+    }
+  };
 
-  // ---- global -> registers for one tile (zeros past kv_end)
-  u32x4 kreg[KCH], vreg[2 * VPR];
-  auto fetch = [&](int t) {
+  // ---- global -> registers for one tile. Every load is issued
+  // unconditionally (positions clamped into [0, kv_end), lanes past the tile
+  // clamped onto its last chunk), so all of a tile's loads are in flight
+  // together; rows past kv_end are zeroed when the tile is staged.
+  u32x4 kreg_a[KCH], vreg_a[2 * VPR], kreg_b[KCH], vreg_b[2 * VPR];
+  auto fetch = [&](u32x4 (&kreg)[KCH], u32x4 (&vreg)[2 * VPR], int t) {
+    window_for(t);
     const int kv0 = t * KT;
 #pragma unroll
     for (int r = 0; r < KCH; ++r) {
-      const int ci = tid + 256 * r;
+      const int ci = min(tid + 256 * r, NKC - 1);
       const int key = ci / CPR, dc = ci % CPR;
-      const int pos = kv0 + key;
-      kreg[r] = u32x4{0u, 0u, 0u, 0u};
-      if (ci < NKC && pos < kv_end)
-        kreg[r] = *reinterpret_cast<const u32x4*>(kc + kv_row_offset(block_of(pos), h, pos % BS, a.H, BS, D) * 2 +
-                                                  dc * 16);
+      const int pos = min(kv0 + key, kv_end - 1);
+      kreg[r] = *reinterpret_cast<const u32x4*>(kc + kv_row_offset(block_of(pos), h, pos % BS, a.H, BS, D) * 2 +
+                                                dc * 16);
     }
 #pragma unroll
     for (int r = 0; r < VPR; ++r) {
-      const int pi = tid + 256 * r;
+      const int pi = min(tid + 256 * r, NVP - 1);
       const int kp = pi / CPR, dc = pi % CPR;
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const int pos = kv0 + 2 * kp + e;
-        vreg[2 * r + e] = u32x4{0u, 0u, 0u, 0u};
-        if (pi < NVP && pos < kv_end)
-          vreg[2 * r + e] = *reinterpret_cast<const u32x4*>(
-              vc + kv_row_offset(block_of(pos), h, pos % BS, a.H, BS, D) * 2 + dc * 16);
+        const int pos = min(kv0 + 2 * kp + e, kv_end - 1);
+        vreg[2 * r + e] = *reinterpret_cast<const u32x4*>(
+            vc + kv_row_offset(block_of(pos), h, pos % BS, a.H, BS, D) * 2 + dc * 16);
       }
     }
   };
   // ---- registers -> LDS buffer b: K row-major, V transposed (two keys packed per word)
-  auto stage = [&](int b) {
+  auto stage = [&](int b, int t, const u32x4 (&kreg)[KCH], const u32x4 (&vreg)[2 * VPR]) {
+    const int kv0 = t * KT;
+    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int r = 0; r < KCH; ++r) {
       const int ci = tid + 256 * r;
-      if (ci < NKC) {
+      if (NKC % 256 == 0 || ci < NKC) {
         const int key = ci / CPR, dc = ci % CPR;
-        *reinterpret_cast<u32x4*>(&sk[b][key * KROW + dc * 8]) = kreg[r];
+        *reinterpret_cast<u32x4*>(&sk[b][key * KROW + dc * 8]) = kv0 + key < kv_end ? kreg[r] : z;
       }
     }
 #pragma unroll
     for (int r = 0; r < VPR; ++r) {
       const int pi = tid + 256 * r;
-      if (pi < NVP) {
+      if (NVP % 256 == 0 || pi < NVP) {
         const int kp = pi / CPR, dc = pi % CPR;
-        const u32x4 v0 = vreg[2 * r], v1 = vreg[2 * r + 1];
+        const u32x4 v0 = kv0 + 2 * kp < kv_end ? vreg[2 * r] : z;
+        const u32x4 v1 = kv0 + 2 * kp + 1 < kv_end ? vreg[2 * r + 1] : z;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const uint32_t lo = (v0[w] & 0xffffu) | (v1[w] << 16);      // element 2w of keys 2kp, 2kp+1
@@ -223,7 +241,14 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
         for (int g = 0; g < NQ; ++g) sacc[g][sub] = mfma<DT>(ka, qf[g][ks], sacc[g][sub]);
       }
     }
-    // online softmax; lane holds query n16, keys kv0 + 16*sub + 4*g4 + i
+    // online softmax; lane holds query n16, keys kv0 + 16*sub + 4*g4 + i.
+    // Only tiles that reach past the wave's first query need the causal
+    // mask (wave-uniform test). The running max is raised lazily: a row
+    // keeps its reference max until a tile's max exceeds it by more than
+    // 2^RESCALE_LOG2, so p = 2^(s - m) stays below 2^RESCALE_LOG2 and the
+    // accumulators are rescaled only on the (rare) tiles where some row
+    // needs it; the final O / l is the same softmax.
+    const bool masked = kv0 + KT - 1 > c0 + wq0;
     u32x4 pb[NQ][NKST];
     u32x4 pbl[NQ][NKST];  // bf16 remainders
 #pragma unroll
@@ -238,14 +263,21 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
         for (int i = 0; i < 4; ++i) {
           const int key = kv0 + 16 * sub + 4 * g4 + i;
           const float x = sacc[g][sub][i] * a.scale_log2;
-          sc[4 * sub + i] = key <= last_key ? x : -INFINITY;
+          sc[4 * sub + i] = (!masked || key <= last_key) ? x : -INFINITY;
           mt = fmaxf(mt, sc[4 * sub + i]);
         }
       mt = fmaxf(mt, shfl_xor_f(mt, 16));
       mt = fmaxf(mt, shfl_xor_f(mt, 32));
-      const float m_new = fmaxf(m[g], mt);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m[g] - m_use);
+      const bool grow = mt > m[g] + RESCALE_LOG2;  // also true for the first tile (m = -inf)
+      if (__any(grow)) {
+        const float m_new = grow ? mt : m[g];
+        const float alpha = __builtin_amdgcn_exp2f(m[g] - m_new);
+        l[g] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[g][dt] *= alpha;
+        m[g] = m_new;
+      }
+      const float m_use = m[g] == -INFINITY ? 0.f : m[g];
       float psum = 0.f;
       uint32_t ph[4 * NSUB], pl[4 * NSUB];
 #pragma unroll
@@ -255,10 +287,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
         ph[i] = to_bits<DT>(p);
         pl[i] = DT == Dt::BF16 ? to_bits<DT>(p - from_bits<DT>(ph[i])) : 0u;
       }
-      l[g] = l[g] * alpha + psum;
-      m[g] = m_new;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[g][dt] *= alpha;
+      l[g] += psum;
       // B operand of O^T += V^T P^T for key step kst: elements 0..3 from
       // subtile 2*kst, 4..7 from subtile 2*kst+1
 #pragma unroll
@@ -288,17 +317,26 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
     }
   };
 
-  // Double-buffered LDS: tile t+1 travels global -> registers while tile t
-  // is computed, then lands in the other buffer; one barrier per tile.
-  fetch(0);
-  stage(0);
+  // Two LDS buffers and two register sets: tile t+2 travels global ->
+  // registers while tile t is computed and tile t+1 (fetched one iteration
+  // earlier) is staged into the other LDS buffer; one barrier per tile.
+  // Even tiles use LDS buffer 0 and register set a, odd tiles buffer 1 and
+  // set b. Fetches and stages are unconditional (past the end they re-read
+  // the last tile, an L2 hit, and stage zeros that are never read) so the
+  // compiler can prove each set's loads were consumed before it is
+  // refilled and never drains the load queue early.
+  fetch(kreg_a, vreg_a, 0);
+  fetch(kreg_b, vreg_b, min(1, n_tiles - 1));
+  stage(0, 0, kreg_a, vreg_a);
   __syncthreads();
-  for (int t = 0; t < n_tiles; ++t) {
-    const bool more = t + 1 < n_tiles;
-    if (more) fetch(t + 1);
-    const int kv0 = t * KT;
-    if (wave_active && kv0 <= wave_last_pos) compute(t & 1, kv0);
-    if (more) stage((t + 1) & 1);
+  for (int t = 0; t < n_tiles; t += 2) {
+    fetch(kreg_a, vreg_a, min(t + 2, n_tiles - 1));
+    if (wave_active && t * KT <= wave_last_pos) compute(0, t * KT);
+    stage(1, t + 1, kreg_b, vreg_b);
+    __syncthreads();
+    fetch(kreg_b, vreg_b, min(t + 3, n_tiles - 1));
+    if (wave_active && t + 1 < n_tiles && (t + 1) * KT <= wave_last_pos) compute(1, (t + 1) * KT);
+    stage(0, t + 2, kreg_a, vreg_a);
     __syncthreads();
   }
 

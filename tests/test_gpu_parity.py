@@ -204,6 +204,26 @@ def test_prefill_parity_small_chunks(dtype, bs):
         assert np.array_equal(bits(host(outn)), bits(rne(host(out32), dtype)))
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("scale", [None, 1.0])
+def test_prefill_long_context_and_wide_scores(dtype, scale):
+    """Contexts past 256 blocks (the kernel's block-table window moves) and,
+    with scale 1, scores spread over hundreds of log2 units (the running max
+    is raised and the accumulators rescaled many times)."""
+    prior, chunk = [4500, 8200, 0], [70, 150, 90]
+    maxb = math.ceil(max(p + c for p, c in zip(prior, chunk)) / 16)
+    wl = prefill_workload(f"pf_long_{dtype}", 705, dtype, 2, 128, 16, prior, chunk, maxb=maxb, pool_factor=1.1,
+                          scale=scale)
+    od = _on_device_written(wl)
+    kc, vc = oracle.reshape_and_cache(wl.new.k, wl.new.v, wl.k_cache, wl.v_cache, wl.new.slot_mapping, 16, dtype)
+    p = wl.prefill
+    ref = oracle.prefill(p.q, kc, vc, p.block_tables, p.context_lens, p.query_start_loc, wl.scale, dtype)
+    got = host(od.prefill(torch.float32)).astype(np.float64)
+    err = np.abs(got - ref).max()
+    assert np.isfinite(got).all()
+    assert err <= ATOL[dtype], f"prefill max abs err {err:.3e}"
+
+
 def test_prefill_config5_sampled_rows_and_decode():
     wl, kc_ref, vc_ref = _config(5)
     od = _on_device_written(wl)
