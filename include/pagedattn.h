@@ -12,9 +12,11 @@
  * blocks in their tables; the kernels only read them.
  *
  * Conventions for every call:
- *  - Tensor pointers are DEVICE pointers owned by the caller. The library
- *    allocates nothing, keeps no pointer after returning, holds no global
- *    mutable state and is safe to call from several host threads.
+ *  - Tensor pointers are DEVICE pointers owned by the caller. The kernel
+ *    calls allocate nothing, keep no pointer after returning, hold no global
+ *    mutable state and are safe to call from several host threads. The
+ *    block allocator (pa_allocator_*) keeps its host-side state in a handle
+ *    the caller creates and destroys.
  *  - Work is queued on `stream` and never synchronised; the library never
  *    reads device memory on the host.
  *  - Validation is host-side on scalars and pointer nullness only; a failed
@@ -47,7 +49,9 @@ typedef enum {
   PA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, inconsistent sizes */
   PA_ERR_UNSUPPORTED = -2, /* head_dim, block_size, dtype or head layout not built */
   PA_ERR_WORKSPACE = -3,   /* split-K workspace missing or too small */
-  PA_ERR_HIP = -4          /* a launch failed; hipGetLastError() was cleared */
+  PA_ERR_HIP = -4,         /* a launch failed; hipGetLastError() was cleared */
+  PA_ERR_NO_BLOCKS = -5,   /* block allocator: not enough free blocks (nothing was changed) */
+  PA_ERR_NO_MEMORY = -6    /* block allocator: host memory allocation failed */
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
@@ -65,14 +69,75 @@ const char* pa_status_string(pa_status status);
  * is left untouched.
  *   k, v          [num_tokens][num_heads][head_dim], dtype
  *   slot_mapping  int32 [num_tokens]
- * Preconditions: non-negative slots are distinct and < num_blocks*block_size.
- * num_tokens == 0 is a no-op. Errors: INVALID_ARG (null pointer, sizes,
+ * Preconditions: non-negative slots are distinct and < num_blocks*block_size
+ * (a slot past the pool is skipped on the device). num_tokens == 0 is a
+ * no-op. Errors: INVALID_ARG (null pointer, sizes,
  * num_blocks*block_size > INT32_MAX), UNSUPPORTED, HIP.
  */
 pa_status pa_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
                                const int32_t* slot_mapping, int32_t num_tokens, int32_t num_heads,
                                int32_t head_dim, int32_t block_size, int32_t num_blocks, pa_dtype dtype,
                                hipStream_t stream);
+
+/*
+ * copy_blocks -- the copy half of copy-on-write. Parallel samples share the
+ * prompt's blocks through their block tables, each block carrying a
+ * reference count; before a sharer writes into a shared block it gets a
+ * private copy (aidocs.cortexgrid.cn page, FAQ answer on parallel
+ * sampling). For every pair i < num_pairs:
+ *   k_cache[map[i][1]] = k_cache[map[i][0]]   (all heads and offsets; same for v)
+ * bit for bit.
+ *   block_mapping  int32 [num_pairs][2] (src, dst), device memory
+ * Preconditions: destinations are distinct and none is also a source (the
+ * copies run concurrently). Pairs naming a block outside [0, num_blocks)
+ * are skipped on the device. num_pairs == 0 is a no-op.
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP.
+ */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping, int32_t num_pairs,
+                         int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                         pa_dtype dtype, hipStream_t stream);
+
+/*
+ * Block allocator -- host-side bookkeeping of the physical blocks (no device
+ * memory is touched). Blocks are handed out on demand as sequences grow and
+ * returned when they finish (devpress page, workflow step on memory
+ * reclamation; betteryeah page, section 2.2); a fork shares every block of
+ * its parent and raises their reference counts; appending to a sequence
+ * whose partly filled last block is shared first moves it to a fresh block
+ * and queues the (old, fresh) pair for pa_copy_blocks (aidocs page, FAQ on
+ * parallel sampling). Free blocks form a LIFO stack that starts with block 0.
+ * The handle is owned by the caller; one host thread at a time per handle.
+ *
+ *   create        num_blocks, block_size > 0, num_blocks*block_size <= INT32_MAX
+ *   new_sequence  returns an empty sequence id (ids are never reused)
+ *   fork          child shares all of parent's blocks (refcount + 1 each)
+ *   append        reserves num_tokens slots at the end of seq and writes their
+ *                 slot ids (block * block_size + offset) to slots (NULL: don't);
+ *                 NO_BLOCKS, with no state changed, if the pool is too small
+ *   free_sequence releases seq's blocks (a block returns to the pool when its
+ *                 count reaches 0); the id becomes invalid
+ *   block_table   copies seq's table into table[capacity] and sets
+ *                 *num_blocks; capacity 0 only queries the size; a smaller
+ *                 non-zero capacity is INVALID_ARG
+ *   take_copies   moves up to capacity pending (src, dst) pairs into
+ *                 pairs[capacity][2], oldest first, and sets *num_pairs;
+ *                 capacity 0 only queries how many are pending
+ *   num_free / refcount / sequence_length return -1 for a bad handle, block or id.
+ * Errors: INVALID_ARG (null pointer, bad id, size), NO_BLOCKS, NO_MEMORY.
+ */
+typedef struct pa_allocator pa_allocator;
+pa_status pa_allocator_create(int32_t num_blocks, int32_t block_size, pa_allocator** out);
+void pa_allocator_destroy(pa_allocator* a);
+int32_t pa_allocator_num_free(const pa_allocator* a);
+int32_t pa_allocator_refcount(const pa_allocator* a, int32_t block);
+pa_status pa_allocator_new_sequence(pa_allocator* a, int32_t* seq);
+pa_status pa_allocator_fork(pa_allocator* a, int32_t parent, int32_t* child);
+pa_status pa_allocator_append(pa_allocator* a, int32_t seq, int32_t num_tokens, int32_t* slots);
+pa_status pa_allocator_free_sequence(pa_allocator* a, int32_t seq);
+int32_t pa_allocator_sequence_length(const pa_allocator* a, int32_t seq);
+pa_status pa_allocator_block_table(const pa_allocator* a, int32_t seq, int32_t* table, int32_t capacity,
+                                   int32_t* num_blocks);
+pa_status pa_allocator_take_copies(pa_allocator* a, int32_t* pairs, int32_t capacity, int32_t* num_pairs);
 
 /*
  * gather_kv -- materialise each sequence's logical K and V contiguously

@@ -5,6 +5,7 @@ benchmark's CPU-baseline leg use this module; the HIP library never does.
 Inputs are the numpy arrays built by ``workloads``; outputs are float64.
 
 * ``reshape_and_cache``: bit copy of new K/V rows into their slots.
+* ``copy_blocks``: bit copy of whole blocks (copy-on-write of shared blocks).
 * ``gather_kv``: raw copy of each sequence's logical K/V through its table.
 * ``decode``: one query per sequence over its ctx cached tokens.
 * ``prefill``: causal query chunks, bottom-right aligned (the chunk is the
@@ -38,11 +39,12 @@ def _open(path: str):
     I = ctypes.c_int
     lib.oracle_widen.argtypes = [P, P, ctypes.c_int64, I]
     lib.oracle_reshape_and_cache.argtypes = [P, P, P, P, P, I, I, I, I, I, I]
+    lib.oracle_copy_blocks.argtypes = [P, P, P, I, I, I, I, I, I]
     lib.oracle_gather_kv.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I]
     lib.oracle_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, ctypes.c_double, I, P, I, I]
     lib.oracle_prefill.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, ctypes.c_double, I, P, I, I]
-    for f in (lib.oracle_widen, lib.oracle_reshape_and_cache, lib.oracle_gather_kv, lib.oracle_decode,
-              lib.oracle_prefill):
+    for f in (lib.oracle_widen, lib.oracle_reshape_and_cache, lib.oracle_copy_blocks, lib.oracle_gather_kv,
+              lib.oracle_decode, lib.oracle_prefill):
         f.restype = ctypes.c_int
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -98,6 +100,16 @@ def reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, block_size: int, dty
     nb, H, bs, D = kc.shape
     assert bs == block_size and k.shape == (T, H, D) and v.shape == (T, H, D)
     _check(_load().oracle_reshape_and_cache(_p(k), _p(v), _p(kc), _p(vc), _p(sm), T, H, D, bs, nb, _DT[dtype]))
+    return kc, vc
+
+
+def copy_blocks(k_cache, v_cache, pairs, dtype: str):
+    """Return copies of the caches where block ``pairs[i, 1]`` holds the bits
+    of block ``pairs[i, 0]`` (both caches, every head and offset)."""
+    kc, vc = k_cache.copy(), v_cache.copy()
+    pr = _c(pairs, np.int32).reshape(-1, 2)
+    nb, H, bs, D = kc.shape
+    _check(_load().oracle_copy_blocks(_p(kc), _p(vc), _p(pr), pr.shape[0], H, D, bs, nb, _DT[dtype]))
     return kc, vc
 
 

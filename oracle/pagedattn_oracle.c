@@ -130,6 +130,41 @@ int oracle_reshape_and_cache(const void* k, const void* v, void* k_cache, void* 
   return O_OK;
 }
 
+/* ---- copy-on-write of whole blocks -------------------------------------- */
+
+/* Parallel sampling shares the prompt's blocks; before a sharer writes into a
+ * shared block, that block is copied to a fresh one (aidocs.cortexgrid.cn
+ * page, FAQ answer on parallel sampling: per-block reference counts and
+ * copy-on-write). For each pair i, block pairs[2i+1] of both caches becomes a
+ * bit copy of block pairs[2i] (all heads, all offsets). Ids out of range, a
+ * destination named twice, or a destination that is also a source (the
+ * result would depend on the order) are rejected before anything is copied. */
+int oracle_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int npairs, int H, int d,
+                       int bs, int num_blocks, int dtype) {
+  if (npairs < 0 || H <= 0 || d <= 0 || bs <= 0 || num_blocks <= 0 || dtype < 0 || dtype > 2)
+    return O_BAD_ARG;
+  if (npairs > 0 && (!k_cache || !v_cache || !pairs)) return O_BAD_ARG;
+  unsigned char* role = calloc((size_t)num_blocks, 1); /* bit 0: source, bit 1: destination */
+  if (!role) return O_NOMEM;
+  for (int i = 0; i < npairs; ++i) {
+    int32_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) { free(role); return O_BAD_BLOCK; }
+    if (role[dst] & 2) { free(role); return O_BAD_ARG; }
+    role[src] |= 1;
+    role[dst] |= 2;
+  }
+  for (int b = 0; b < num_blocks; ++b)
+    if (role[b] == 3) { free(role); return O_BAD_ARG; }
+  free(role);
+  const size_t block_bytes = (size_t)H * bs * d * (size_t)elt_bytes(dtype);
+  for (int i = 0; i < npairs; ++i) {
+    size_t src = (size_t)pairs[2 * i] * block_bytes, dst = (size_t)pairs[2 * i + 1] * block_bytes;
+    memcpy((char*)k_cache + dst, (const char*)k_cache + src, block_bytes);
+    memcpy((char*)v_cache + dst, (const char*)v_cache + src, block_bytes);
+  }
+  return O_OK;
+}
+
 /* ---- block-table translation -------------------------------------------- */
 
 static int check_tables(const int32_t* bt, const int32_t* ctx, int S, int bs, int num_blocks,

@@ -8,6 +8,9 @@ missing library raises.
 Calls mirror the C ABI in ``include/pagedattn.h``:
 
 * ``reshape_and_cache(k, v, k_cache, v_cache, slot_mapping)``
+* ``copy_blocks(k_cache, v_cache, block_mapping)`` and ``BlockAllocator``
+  (host block manager: on-demand blocks, fork with reference counts,
+  copy-on-write, free)
 * ``paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, ...)``
 * ``paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale, ...)``
 * ``gather_kv(...)``, ``decode_workspace_bytes(...)`` and the two decode stages.
@@ -25,6 +28,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = 0, -1, -2, -3, -4
+PA_ERR_NO_BLOCKS, PA_ERR_NO_MEMORY = -5, -6
 _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 _lib = None
 
@@ -58,6 +62,26 @@ def lib():
         L.pa_paged_attention_decode_reduce.argtypes = [P, ctypes.c_int, P, I, I, I, I, ctypes.c_int, P, Z, P]
         L.pa_paged_attention_prefill.argtypes = [P, ctypes.c_int, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F,
                                                  ctypes.c_int, P]
+        L.pa_copy_blocks.argtypes = [P, P, P, I, I, I, I, I, ctypes.c_int, P]
+        PI = ctypes.POINTER(ctypes.c_int32)
+        L.pa_allocator_create.argtypes = [I, I, ctypes.POINTER(P)]
+        L.pa_allocator_destroy.argtypes = [P]
+        L.pa_allocator_destroy.restype = None
+        L.pa_allocator_num_free.argtypes = [P]
+        L.pa_allocator_refcount.argtypes = [P, I]
+        L.pa_allocator_new_sequence.argtypes = [P, PI]
+        L.pa_allocator_fork.argtypes = [P, I, PI]
+        L.pa_allocator_append.argtypes = [P, I, I, P]
+        L.pa_allocator_free_sequence.argtypes = [P, I]
+        L.pa_allocator_sequence_length.argtypes = [P, I]
+        L.pa_allocator_block_table.argtypes = [P, I, P, I, PI]
+        L.pa_allocator_take_copies.argtypes = [P, P, I, PI]
+        for name in ("pa_allocator_num_free", "pa_allocator_refcount", "pa_allocator_sequence_length"):
+            getattr(L, name).restype = I
+        for name in ("pa_copy_blocks", "pa_allocator_create", "pa_allocator_new_sequence", "pa_allocator_fork",
+                     "pa_allocator_append", "pa_allocator_free_sequence", "pa_allocator_block_table",
+                     "pa_allocator_take_copies"):
+            getattr(L, name).restype = ctypes.c_int
         for name in ("pa_reshape_and_cache", "pa_gather_kv", "pa_paged_attention_decode",
                      "pa_paged_attention_decode_partitions", "pa_paged_attention_decode_reduce",
                      "pa_paged_attention_prefill"):
@@ -112,6 +136,97 @@ def reshape_and_cache(k, v, k_cache, v_cache, slot_mapping):
     _check("reshape_and_cache", lib().pa_reshape_and_cache(
         _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), T, H, D, bs, nb,
         _DT[k_cache.dtype], _stream()))
+
+
+def copy_blocks(k_cache, v_cache, block_mapping):
+    """Copy-on-write: block ``block_mapping[i, 1]`` of both caches becomes a
+    copy of block ``block_mapping[i, 0]`` (int32 ``[pairs, 2]`` on the GPU)."""
+    _dev(k_cache, v_cache, block_mapping)
+    _i32(block_mapping)
+    nb, H, bs, D = _cache_dims(k_cache, v_cache)
+    if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [num_pairs, 2]")
+    _check("copy_blocks", lib().pa_copy_blocks(
+        _ptr(k_cache), _ptr(v_cache), _ptr(block_mapping), int(block_mapping.shape[0]), H, D, bs, nb,
+        _DT[k_cache.dtype], _stream()))
+
+
+class BlockAllocator:
+    """Host block manager of the library (``pa_allocator_*``): blocks on
+    demand, forks sharing blocks with reference counts, copy-on-write of a
+    shared partly filled last block, release on free. Sequence ids are ints."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        h = ctypes.c_void_p()
+        _check("allocator_create", lib().pa_allocator_create(int(num_blocks), int(block_size), ctypes.byref(h)))
+        self._h = h
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+
+    def close(self):
+        if self._h:
+            lib().pa_allocator_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def num_free(self) -> int:
+        return int(lib().pa_allocator_num_free(self._h))
+
+    def refcount(self, block: int) -> int:
+        return int(lib().pa_allocator_refcount(self._h, int(block)))
+
+    def new_sequence(self) -> int:
+        sid = ctypes.c_int32()
+        _check("allocator_new_sequence", lib().pa_allocator_new_sequence(self._h, ctypes.byref(sid)))
+        return sid.value
+
+    def fork(self, parent: int) -> int:
+        sid = ctypes.c_int32()
+        _check("allocator_fork", lib().pa_allocator_fork(self._h, int(parent), ctypes.byref(sid)))
+        return sid.value
+
+    def append(self, seq: int, num_tokens: int):
+        """Slots (``block * block_size + offset``) of ``num_tokens`` new
+        tokens at the end of ``seq``, as an int32 numpy array."""
+        import numpy as np
+        slots = np.zeros(max(0, int(num_tokens)), dtype=np.int32)
+        _check("allocator_append", lib().pa_allocator_append(self._h, int(seq), int(num_tokens),
+                                                                slots.ctypes.data_as(ctypes.c_void_p)))
+        return slots
+
+    def free(self, seq: int) -> None:
+        _check("allocator_free_sequence", lib().pa_allocator_free_sequence(self._h, int(seq)))
+
+    def length(self, seq: int) -> int:
+        return int(lib().pa_allocator_sequence_length(self._h, int(seq)))
+
+    def block_table(self, seq: int):
+        import numpy as np
+        n = ctypes.c_int32()
+        _check("allocator_block_table", lib().pa_allocator_block_table(self._h, int(seq), None, 0, ctypes.byref(n)))
+        t = np.zeros(n.value, dtype=np.int32)
+        if n.value:
+            _check("allocator_block_table", lib().pa_allocator_block_table(
+                self._h, int(seq), t.ctypes.data_as(ctypes.c_void_p), n.value, ctypes.byref(n)))
+        return t
+
+    def take_copies(self):
+        """Pending copy-on-write (src, dst) block pairs, oldest first, as an
+        int32 ``[n, 2]`` numpy array; the queue is emptied."""
+        import numpy as np
+        n = ctypes.c_int32()
+        _check("allocator_take_copies", lib().pa_allocator_take_copies(self._h, None, 0, ctypes.byref(n)))
+        out = np.zeros((n.value, 2), dtype=np.int32)
+        if n.value:
+            _check("allocator_take_copies", lib().pa_allocator_take_copies(
+                self._h, out.ctypes.data_as(ctypes.c_void_p), n.value, ctypes.byref(n)))
+        return out
 
 
 def gather_kv(k_out, v_out, k_cache, v_cache, block_tables, context_lens, cu_context_lens, max_context_len: int):

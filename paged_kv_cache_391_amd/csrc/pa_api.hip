@@ -96,6 +96,8 @@ const char* pa_status_string(pa_status status) {
     case PA_ERR_UNSUPPORTED: return "unsupported configuration";
     case PA_ERR_WORKSPACE: return "split-K workspace missing, misaligned or too small";
     case PA_ERR_HIP: return "HIP launch failure";
+    case PA_ERR_NO_BLOCKS: return "no free KV block left in the pool";
+    case PA_ERR_NO_MEMORY: return "host memory allocation failed";
   }
   return "unknown status";
 }
@@ -110,7 +112,21 @@ pa_status pa_reshape_and_cache(const void* k, const void* v, void* k_cache, void
   if (num_tokens == 0) return PA_OK;
   if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PA_ERR_INVALID_ARG;
   return hip_status(pa::launch_reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, num_tokens, num_heads,
-                                                 head_dim, block_size, elt_bytes(dtype), stream));
+                                                 head_dim, block_size, num_blocks, elt_bytes(dtype), stream));
+}
+
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping, int32_t num_pairs,
+                         int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                         pa_dtype dtype, hipStream_t stream) {
+  pa_status st = check_cache_shape(num_heads, head_dim, block_size, num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) return PA_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_mapping) return PA_ERR_INVALID_ARG;
+  const int64_t wgs = ((int64_t)num_heads * block_size * head_dim * elt_bytes(dtype) / 16 + 1023) / 1024;
+  if ((int64_t)num_pairs * wgs > INT32_MAX) return PA_ERR_INVALID_ARG;
+  return hip_status(pa::launch_copy_blocks(k_cache, v_cache, block_mapping, num_pairs, num_heads, head_dim,
+                                           block_size, num_blocks, elt_bytes(dtype), stream));
 }
 
 pa_status pa_gather_kv(void* k_out, void* v_out, const void* k_cache, const void* v_cache,

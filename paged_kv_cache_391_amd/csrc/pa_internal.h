@@ -46,8 +46,10 @@ struct DecodeArgs {
 };
 
 hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
-                                    const int32_t* slot_mapping, int T, int H, int D, int BS, int elt_bytes,
-                                    hipStream_t stream);
+                                    const int32_t* slot_mapping, int T, int H, int D, int BS, int num_blocks,
+                                    int elt_bytes, hipStream_t stream);
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping, int num_pairs, int H,
+                              int D, int BS, int num_blocks, int elt_bytes, hipStream_t stream);
 hipError_t launch_gather_kv(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
                             const int32_t* block_tables, const int32_t* context_lens, const int32_t* cu_ctx,
                             int S, int max_ctx, int H, int D, int BS, int max_blocks, int elt_bytes,

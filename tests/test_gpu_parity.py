@@ -52,6 +52,75 @@ def test_reshape_and_cache_bit_exact(cid):
     assert np.array_equal(bits(host(od.v_cache)), bits(vc_ref))
 
 
+@pytest.mark.parametrize("dtype,H,D,bs", [("f16", 40, 128, 16), ("bf16", 32, 128, 32), ("f32", 2, 64, 16)])
+def test_copy_blocks_bit_exact(dtype, H, D, bs):
+    """Copy-on-write block copies equal the oracle's bit for bit; blocks that
+    are not destinations keep their bits; a pair naming a block outside the
+    pool is skipped by the kernel's own bounds check."""
+    rng = np.random.default_rng(21)
+    nb = 64
+    from workloads import normal
+    kc = normal(rng, (nb, H, bs, D), dtype)
+    vc = normal(rng, (nb, H, bs, D), dtype)
+    perm = rng.permutation(nb)
+    pairs = np.stack([perm[:20], perm[20:40]], 1).astype(np.int32)
+    kref, vref = oracle.copy_blocks(kc, vc, pairs, dtype)
+    dk, dv = dev(kc, dtype), dev(vc, dtype)
+    pa.copy_blocks(dk, dv, dev(pairs))
+    assert np.array_equal(bits(host(dk)), bits(kref)) and np.array_equal(bits(host(dv)), bits(vref))
+    outside = np.array([[perm[40], nb], [nb + 5, perm[41]]], dtype=np.int32)
+    pa.copy_blocks(dk, dv, dev(outside))
+    assert np.array_equal(bits(host(dk)), bits(kref)) and np.array_equal(bits(host(dv)), bits(vref))
+    pa.copy_blocks(dk, dv, dev(np.zeros((0, 2), dtype=np.int32)))
+    torch.cuda.synchronize()
+
+
+def test_copy_on_write_with_the_native_allocator_then_decode():
+    """Parallel sampling end to end: the library's allocator forks a 37-token
+    prompt into 4 samples; each sample's next tokens trigger a copy of the
+    shared partly filled block; the copies run on the GPU, the new tokens are
+    written, and decode over all samples matches the oracle fed the same
+    tables, copies and writes."""
+    H, D, bs, dtype, nb = 8, 128, 16, "f16", 48
+    rng = np.random.default_rng(22)
+    from workloads import normal
+    alloc = pa.BlockAllocator(nb, bs)
+    prompt = alloc.new_sequence()
+    prompt_slots = alloc.append(prompt, 37)
+    samples = [prompt] + [alloc.fork(prompt) for _ in range(3)]
+    kc = normal(rng, (nb, H, bs, D), dtype)
+    vc = normal(rng, (nb, H, bs, D), dtype)
+    pk, pv = normal(rng, (37, H, D), dtype), normal(rng, (37, H, D), dtype)
+    kc, vc = oracle.reshape_and_cache(pk, pv, kc, vc, prompt_slots, bs, dtype)
+    new_slots, copies = [], []
+    for i, sq in enumerate(samples[::-1]):           # the prompt itself writes last, in place
+        new_slots.append(alloc.append(sq, 2 + 7 * i))
+        copies.append(alloc.take_copies())
+    copies = np.concatenate(copies)
+    assert copies.shape[0] == 3 and len(set(copies[:, 1])) == 3
+    slots = np.concatenate(new_slots)
+    nk, nv = normal(rng, (slots.size, H, D), dtype), normal(rng, (slots.size, H, D), dtype)
+    tables = [alloc.block_table(sq) for sq in samples]
+    maxb = max(t.size for t in tables)
+    bt = np.full((4, maxb), -1, dtype=np.int32)
+    for i, t in enumerate(tables):
+        bt[i, :t.size] = t
+    ctx = np.array([alloc.length(sq) for sq in samples], dtype=np.int32)
+    q = normal(rng, (4, H, D), dtype)
+    scale = 1 / math.sqrt(D)
+    rk, rv = oracle.copy_blocks(kc, vc, copies, dtype)
+    rk, rv = oracle.reshape_and_cache(nk, nv, rk, rv, slots, bs, dtype)
+    ref = oracle.decode(q, rk, rv, bt, ctx, scale, dtype)
+    dk, dv = dev(kc, dtype), dev(vc, dtype)
+    pa.copy_blocks(dk, dv, dev(copies))
+    pa.reshape_and_cache(dev(nk, dtype), dev(nv, dtype), dk, dv, dev(slots))
+    assert np.array_equal(bits(host(dk)), bits(rk)) and np.array_equal(bits(host(dv)), bits(rv))
+    out = torch.empty((4, H, D), dtype=torch.float32, device="cuda")
+    ws = pa.make_decode_workspace(4, H, D, int(ctx.max()))
+    pa.paged_attention_decode(out, dev(q, dtype), dk, dv, dev(bt), dev(ctx), scale, int(ctx.max()), ws)
+    _check_attention(out, ref, dtype)
+
+
 @pytest.mark.parametrize("cid", [1, 3, 4])
 def test_gather_kv_bit_exact(cid):
     wl, kc_ref, vc_ref = _config(cid)

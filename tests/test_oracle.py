@@ -353,3 +353,30 @@ def test_out_of_range_block_id_is_rejected():
     bt[0, 1] = 3
     with pytest.raises(oracle.OracleError):
         oracle.decode(wl.decode.q, wl.k_cache, wl.v_cache, bt, wl.decode.context_lens, 1.0, "f32")
+
+
+def test_copy_blocks_matches_numpy_block_assignment_and_rejects_ambiguous_maps():
+    """Copy-on-write copies: block dst of both caches equals block src bit for
+    bit, every other block is untouched (numpy fancy-index assignment is the
+    independent reference); a destination named twice, a destination that is
+    also a source, and ids outside the pool are rejected."""
+    rng = np.random.default_rng(11)
+    for dtype, shape in (("f16", (12, 3, 16, 64)), ("bf16", (9, 2, 32, 128)), ("f32", (7, 2, 16, 64))):
+        n = int(np.prod(shape))
+        kc = (rng.integers(0, 1 << 16, n, dtype=np.uint32).astype(np.uint16) if dtype != "f32"
+              else rng.standard_normal(n).astype(np.float32)).reshape(shape)
+        if dtype == "f16":
+            kc = kc.view(np.float16)
+        vc = kc[::-1].copy()
+        perm = rng.permutation(shape[0])
+        pairs = np.stack([perm[:3], perm[3:6]], 1).astype(np.int32)
+        k2, v2 = oracle.copy_blocks(kc, vc, pairs, dtype)
+        ek, ev = kc.copy(), vc.copy()
+        ek[pairs[:, 1]] = kc[pairs[:, 0]]
+        ev[pairs[:, 1]] = vc[pairs[:, 0]]
+        view = {"f16": np.uint16, "bf16": np.uint16, "f32": np.uint32}[dtype]
+        assert np.array_equal(k2.view(view), ek.view(view)) and np.array_equal(v2.view(view), ev.view(view))
+        assert not np.array_equal(k2.view(view), kc.view(view))
+        for bad in ([[0, 1], [2, 1]], [[0, 1], [1, 2]], [[0, shape[0]]], [[-1, 1]]):
+            with pytest.raises(oracle.OracleError):
+                oracle.copy_blocks(kc, vc, bad, dtype)

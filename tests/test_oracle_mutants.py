@@ -30,6 +30,10 @@ MUTANTS = {
     "bf16_shift": ("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
     "slot_block_offset_swapped": ("int64_t blk = s / bs, off = s % bs;", "int64_t blk = s % bs, off = s / bs;"),
     "duplicate_slots_accepted": ("if (seen[s]) { free(seen); return O_DUP_SLOT; }", ""),
+    "copy_source_and_destination_swapped": (
+        "size_t src = (size_t)pairs[2 * i] * block_bytes, dst = (size_t)pairs[2 * i + 1] * block_bytes;",
+        "size_t dst = (size_t)pairs[2 * i] * block_bytes, src = (size_t)pairs[2 * i + 1] * block_bytes;"),
+    "copy_of_values_skipped": ("memcpy((char*)v_cache + dst, (const char*)v_cache + src, block_bytes);", ""),
 }
 
 PINS = [
@@ -45,6 +49,7 @@ PINS = [
     (pins.test_reshape_and_cache_round_trip_and_untouched_slots, ()),
     (pins.test_reshape_and_cache_skips_negative_and_rejects_bad_slots, ()),
     (pins.test_gather_matches_independent_index_arithmetic, ()),
+    (pins.test_copy_blocks_matches_numpy_block_assignment_and_rejects_ambiguous_maps, ()),
 ]
 
 
