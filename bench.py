@@ -10,7 +10,10 @@ Other workloads (``--workload``), same machinery:
   mixed256    256 sequences x 32 x 128, bf16, block_size 32, lognormal
               context lengths (mean ~600, clipped to [1, 4096]), 1.25x pool
   prefix13b   32 prompts x 8 samples, 40 x 128, f16, block_size 16, a
-              1024-token prompt whose blocks all 8 samples share, tails U[0,256]
+              1024-token prompt whose blocks all 8 samples share, tails U[0,256];
+              decoded by the shared-prefix call (each shared tile read once
+              per prompt; --plain: the ordinary decode), so its algorithmic
+              bytes count each aliased K/V byte once
   mixed_step  40 x 128, f16, block_size 16: cache write of 2048 rows, causal
               prefill of 4 chunks (L ~ U[256,512] after U[0,1024] cached
               tokens) and decode of 96 sequences (ctx ~ U[256,4096])
@@ -163,14 +166,14 @@ def prefill_work(p, H, D, elt):
     return flops, byts
 
 
-def cpu_baseline(wl, threads):
+def cpu_baseline(wl, threads, alg_bytes):
     """The fp64 oracle, as it stands, over the same decode (and prefill)
-    work, repeated until about CPU_SECONDS have elapsed."""
+    work, repeated until about CPU_SECONDS have elapsed; its rate uses the
+    same algorithmic byte count as the GPU step's value."""
     import oracle
     kc, vc = oracle.reshape_and_cache(wl.new.k, wl.new.v, wl.k_cache, wl.v_cache, wl.new.slot_mapping,
                                       wl.block_size, wl.dtype)
     d, p = wl.decode, wl.prefill
-    H, D, elt, bs = wl.num_heads, wl.head_dim, wl.elt_bytes, wl.block_size
 
     def one_pass():
         if p is not None:
@@ -186,8 +189,7 @@ def cpu_baseline(wl, threads):
         if el >= CPU_SECONDS or reps >= 1000:
             break
     per = el / reps
-    kv, table, qo = decode_bytes(d.context_lens, H, D, elt, bs)
-    byts = kv + table + qo + (prefill_work(p, H, D, elt)[1] if p is not None else 0)
+    byts = alg_bytes
     what = "prefill of the 4 chunks + decode" if p is not None else "the whole decode"
     return {"value": round(byts / per / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{what} of this workload, {reps} pass(es) in {el:.1f} s ({per:.3f} s each); fp64, gather + "
@@ -202,6 +204,7 @@ def main():
     ap.add_argument("--workload", choices=list(WORKLOADS), default="llama7b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--plain", action="store_true", help="prefix13b: ordinary decode instead of the shared-prefix call")
     ap.add_argument("--copy-probe-gib", type=float, default=1.0, help="size of the plain-copy bandwidth probe")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="store HBM bytes per launch from two rocprofv3 --pmc runs of this script and exit")
@@ -232,7 +235,16 @@ def main():
     d, p = wl.decode, wl.prefill
     S, H, D, bs, elt = d.num_seqs, wl.num_heads, wl.head_dim, wl.block_size, wl.elt_bytes
     maxctx = d.max_context_len
-    ws = pa.make_decode_workspace(S, H, D, maxctx)
+    shared = args.workload == "prefix13b" and not args.plain
+    if shared:
+        # samples of one prompt are consecutive rows sharing the prompt's whole blocks
+        nsamp = len(wl.notes["tails"][0])
+        gs = torch.arange(0, S + 1, nsamp, dtype=torch.int32, device="cuda")
+        pl = torch.tensor([(p // bs) * bs for p in wl.notes["prompt_lens"]], dtype=torch.int32, device="cuda")
+        max_prefix = int(pl.max().item())
+        ws = pa.make_decode_shared_workspace(S, H, D, maxctx)
+    else:
+        ws = pa.make_decode_workspace(S, H, D, maxctx)
     out = torch.empty_like(od.q)  # output in the input dtype: the production path
     pf_out = torch.empty_like(od.pf_q) if p is not None else None
     P = pa.decode_partition_tokens()
@@ -249,13 +261,20 @@ def main():
                                        max_context_len=p.max_context_len)
         if ev is not None:
             ev[2].record()
-        pa.paged_attention_decode_partitions(out, od.q, od.k_cache, od.v_cache, od.block_tables, od.context_lens,
-                                             wl.scale, maxctx, ws)
-        if ev is not None:
-            ev[3].record()
-        pa.paged_attention_decode_reduce(out, od.context_lens, D, maxctx, od.q.dtype, ws)
-        if ev is not None:
-            ev[4].record()
+        if shared:
+            pa.paged_attention_decode_shared_prefix(out, od.q, od.k_cache, od.v_cache, od.block_tables,
+                                                    od.context_lens, gs, pl, wl.scale, maxctx, nsamp, max_prefix, ws)
+            if ev is not None:
+                ev[3].record()
+                ev[4].record()
+        else:
+            pa.paged_attention_decode_partitions(out, od.q, od.k_cache, od.v_cache, od.block_tables,
+                                                 od.context_lens, wl.scale, maxctx, ws)
+            if ev is not None:
+                ev[3].record()
+            pa.paged_attention_decode_reduce(out, od.context_lens, D, maxctx, od.q.dtype, ws)
+            if ev is not None:
+                ev[4].record()
 
     # ---- algorithmic work (valid tokens only)
     kv, table, qo = decode_bytes(d.context_lens, H, D, elt, bs)
@@ -264,6 +283,11 @@ def main():
     cache_write_bytes = 4 * t_valid * H * D * elt + 4 * T
     k2_bytes = partition_kernel_bytes(d.context_lens, H, D, elt, bs, P)
     pf_flops, pf_bytes = prefill_work(p, H, D, elt) if p is not None else (0, 0)
+    logical_kv = kv
+    if args.workload == "prefix13b":
+        kv = unique_kv_bytes(d.block_tables, d.context_lens, H, D, elt, bs)  # each aliased byte once
+        if shared:
+            k2_bytes = kv + table + qo  # the whole shared-prefix call: distinct K/V, table, q and out
     step_bytes = kv + table + qo + cache_write_bytes + pf_bytes
 
     # eager pass: HIP events on the launch stream around every kernel launch
@@ -353,7 +377,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, max(1, min(16, os.cpu_count() or 1)))
+        cpu = cpu_baseline(wl, max(1, min(16, os.cpu_count() or 1)), kv + table + qo + pf_bytes)
 
     rec = {
         "metric": METRIC if args.workload == "llama7b" else METRIC_OTHER,
@@ -372,9 +396,10 @@ def main():
                    "partition_tokens": P, "parallelism": "none (1 GPU)"},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(k2_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(k2_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": f"decode_partition_kernel<{wl.dtype},{D},{bs}>", "bytes_per_launch": k2_bytes,
-                     "avg_launch_us": round(k2_ms * 1e3, 2)},
+                     "frac": round(k2_gbps / HBM_PEAK_GBPS, 4), "traffic": None if shared else traffic,
+                     "kernel": ("shared-prefix decode call (shared, tail and reduction kernels)" if shared
+                                else f"decode_partition_kernel<{wl.dtype},{D},{bs}>"),
+                     "bytes_per_launch": k2_bytes, "avg_launch_us": round(k2_ms * 1e3, 2)},
         "timing": "hip_graph_replay" if not args.eager else "eager",
         "eager_ms_per_step": round(eager_ms, 5),
         "hbm_copy_probe_GBps": round(copy_gbps, 1),
@@ -384,10 +409,10 @@ def main():
         "cpu_baseline": cpu,
     }
     if args.workload == "prefix13b":
-        uniq = unique_kv_bytes(d.block_tables, d.context_lens, H, D, elt, bs)
-        rec["aliasing"] = {"logical_kv_bytes": kv, "unique_kv_bytes": uniq,
-                           "logical_GBps": round(kv / (k2_ms * 1e-3) / 1e9, 1),
-                           "unique_GBps": round(uniq / (k2_ms * 1e-3) / 1e9, 1)}
+        rec["aliasing"] = {"path": "shared-prefix decode" if shared else "plain decode",
+                           "logical_kv_bytes": logical_kv, "unique_kv_bytes": kv,
+                           "logical_GBps": round(logical_kv / (k2_ms * 1e-3) / 1e9, 1),
+                           "unique_GBps": round(kv / (k2_ms * 1e-3) / 1e9, 1)}
     if p is not None:
         pf_tflops = pf_flops / (pf_ms * 1e-3) / 1e12
         rec["phases_us"]["prefill"] = round(pf_ms * 1e3, 2)

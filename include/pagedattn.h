@@ -213,6 +213,43 @@ pa_status pa_paged_attention_decode_reduce(void* out, pa_dtype out_dtype, const 
                                            size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * paged_attention_decode_shared_prefix -- decode for batches in which groups
+ * of sequences share a prefix through aliased blocks, as the samples of one
+ * prompt do in parallel sampling (aidocs.cortexgrid.cn page, intro bullets
+ * and FAQ answer on parallel sampling; devpress page, "实际收益远超预期").
+ * Computes exactly what pa_paged_attention_decode computes, but reads each
+ * shared K/V tile once per group instead of once per sequence: one wave
+ * scores the queries of up to 8 group members against every shared tile,
+ * each member's private tail runs as ordinary split-K partitions, and the
+ * reduction merges both.
+ *   group_starts  int32 [num_groups+1], device: rows group_starts[g] ..
+ *                 group_starts[g+1]-1 form group g; group_starts[0] == 0,
+ *                 non-decreasing, group_starts[num_groups] == num_seqs
+ *   prefix_lens   int32 [num_groups], device: tokens every member of group
+ *                 g holds in the same physical blocks (identical first
+ *                 prefix_lens[g]/block_size table entries); a multiple of
+ *                 block_size, <= every member's context length; 0 = nothing
+ *                 shared (a group of one sequence)
+ *   max_group_size >= every group's size; max_prefix_len >= every prefix
+ *   workspace     required: >= pa_decode_shared_workspace_bytes(...) bytes,
+ *                 16-byte aligned (fp32 partials of the shared and private
+ *                 partitions)
+ * Other arguments and layouts as for pa_paged_attention_decode. f32 caches
+ * run the ordinary decode (same result). A prefix longer than a member's
+ * context is clamped on the device (no read past that member's blocks).
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
+ */
+size_t pa_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                        int32_t max_context_len);
+pa_status pa_paged_attention_decode_shared_prefix(
+    void* out, pa_dtype out_dtype, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* group_starts,
+    const int32_t* prefix_lens, int32_t num_groups, int32_t max_group_size, int32_t max_prefix_len,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, float scale, pa_dtype dtype,
+    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * paged_attention_prefill -- causal attention of multi-token query chunks
  * over the paged cache. Sequence s owns query rows query_start_loc[s] ..
  * query_start_loc[s+1]-1 (L_s >= 0 of them); its context context_lens[s]

@@ -63,6 +63,11 @@ def lib():
         L.pa_paged_attention_prefill.argtypes = [P, ctypes.c_int, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F,
                                                  ctypes.c_int, P]
         L.pa_copy_blocks.argtypes = [P, P, P, I, I, I, I, I, ctypes.c_int, P]
+        L.pa_decode_shared_workspace_bytes.argtypes = [I, I, I, I]
+        L.pa_decode_shared_workspace_bytes.restype = Z
+        L.pa_paged_attention_decode_shared_prefix.argtypes = [P, ctypes.c_int, P, P, P, P, P, P, P, I, I, I, I, I, I,
+                                                              I, I, I, I, I, F, ctypes.c_int, P, Z, P]
+        L.pa_paged_attention_decode_shared_prefix.restype = ctypes.c_int
         PI = ctypes.POINTER(ctypes.c_int32)
         L.pa_allocator_create.argtypes = [I, I, ctypes.POINTER(P)]
         L.pa_allocator_destroy.argtypes = [P]
@@ -279,6 +284,32 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     split-K over long contexts. Pass ``max_context_len`` to avoid a sync."""
     _check("paged_attention_decode", lib().pa_paged_attention_decode(
         *_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, workspace)))
+
+
+def decode_shared_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int) -> int:
+    return int(lib().pa_decode_shared_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len))
+
+
+def make_decode_shared_workspace(num_seqs, num_heads, head_dim, max_context_len, device="cuda"):
+    n = decode_shared_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len)
+    return torch.empty(max(1, n // 4), dtype=torch.float32, device=device)
+
+
+def paged_attention_decode_shared_prefix(out, q, k_cache, v_cache, block_tables, context_lens, group_starts,
+                                         prefix_lens, scale: float, max_context_len: int, max_group_size: int,
+                                         max_prefix_len: int, workspace):
+    """Decode where the rows ``group_starts[g]:group_starts[g+1]`` share their
+    first ``prefix_lens[g]`` tokens through aliased blocks; each shared tile is
+    read once per group. Same result as ``paged_attention_decode``."""
+    _dev(group_starts, prefix_lens)
+    _i32(group_starts, prefix_lens)
+    G = int(prefix_lens.shape[0])
+    if group_starts.shape != (G + 1,):
+        raise ValueError("group_starts must be [num_groups + 1]")
+    args = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, workspace)
+    # (out, odt, q, kc, vc, bt, ctx, S, H, KVH, D, bs, nb, maxb, maxctx, scale, dt, ws, wsb, stream)
+    _check("paged_attention_decode_shared_prefix", lib().pa_paged_attention_decode_shared_prefix(
+        *args[:7], _ptr(group_starts), _ptr(prefix_lens), G, int(max_group_size), int(max_prefix_len), *args[7:]))
 
 
 def paged_attention_decode_partitions(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,

@@ -74,6 +74,7 @@ pa_status prepare_decode(DecodeCall& call, void* out, pa_dtype out_dtype, const 
   a.H = num_heads;
   a.max_blocks = max_blocks_per_seq;
   a.max_parts = (int)grid_parts;
+  a.ws_parts = (int)grid_parts;
   // without split-K one partition spans the longest context
   a.part_tiles = split ? pa::kPartitionTokens / 16 : (int)std::max<int64_t>(1, ceil_div(max_context_len, 16));
   a.scale_log2 = scale * 1.4426950408889634f;
@@ -170,7 +171,7 @@ pa_status pa_paged_attention_decode_partitions(void* out, pa_dtype out_dtype, co
                                 num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                                 max_context_len, scale, dtype, workspace, workspace_bytes);
   if (st != PA_OK || num_seqs == 0) return st;
-  return hip_status(pa::launch_decode_partitions(call.args, call.dt, call.D, call.BS, false, stream));
+  return hip_status(pa::launch_decode_partitions(call.args, call.dt, call.D, call.BS, pa::RowMode::Decode, stream));
 }
 
 pa_status pa_paged_attention_decode_reduce(void* out, pa_dtype out_dtype, const int32_t* context_lens,
@@ -193,9 +194,10 @@ pa_status pa_paged_attention_decode_reduce(void* out, pa_dtype out_dtype, const 
   a.num_seqs = num_seqs;
   a.H = num_heads;
   a.max_parts = (int)parts;
+  a.ws_parts = (int)parts;
   a.part_tiles = pa::kPartitionTokens / 16;
   a.out_f32 = out_dtype == PA_F32 ? 1 : 0;
-  return hip_status(pa::launch_decode_reduce(a, static_cast<Dt>(dtype), head_dim, stream));
+  return hip_status(pa::launch_decode_reduce(a, static_cast<Dt>(dtype), head_dim, false, stream));
 }
 
 pa_status pa_paged_attention_decode(void* out, pa_dtype out_dtype, const void* q, const void* k_cache,
@@ -210,8 +212,79 @@ pa_status pa_paged_attention_decode(void* out, pa_dtype out_dtype, const void* q
                                 num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                                 max_context_len, scale, dtype, workspace, workspace_bytes);
   if (st != PA_OK || num_seqs == 0) return st;
-  hipError_t e = pa::launch_decode_partitions(call.args, call.dt, call.D, call.BS, false, stream);
-  if (e == hipSuccess && call.split) e = pa::launch_decode_reduce(call.args, call.dt, call.D, stream);
+  hipError_t e = pa::launch_decode_partitions(call.args, call.dt, call.D, call.BS, pa::RowMode::Decode, stream);
+  if (e == hipSuccess && call.split) e = pa::launch_decode_reduce(call.args, call.dt, call.D, false, stream);
+  return hip_status(e);
+}
+
+size_t pa_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                        int32_t max_context_len) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+  const int64_t slots = max_parts_for(max_context_len) + 1;  // shared + own partitions of one row
+  return (size_t)num_seqs * num_heads * slots * (head_dim + 2) * sizeof(float);
+}
+
+pa_status pa_paged_attention_decode_shared_prefix(
+    void* out, pa_dtype out_dtype, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* group_starts,
+    const int32_t* prefix_lens, int32_t num_groups, int32_t max_group_size, int32_t max_prefix_len,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, float scale, pa_dtype dtype,
+    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  pa_status st = check_cache_shape(num_heads, head_dim, block_size, num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || num_groups < 0 || max_group_size < 0 ||
+      max_prefix_len < 0 || max_prefix_len > max_context_len)
+    return PA_ERR_INVALID_ARG;
+  if (num_kv_heads != num_heads) return PA_ERR_UNSUPPORTED;
+  if (out_dtype != PA_F32 && out_dtype != dtype) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (num_groups < 1 || num_groups > num_seqs || max_group_size < 1 || max_group_size > num_seqs)
+    return PA_ERR_INVALID_ARG;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !group_starts || !prefix_lens)
+    return PA_ERR_INVALID_ARG;
+  const size_t need = pa_decode_shared_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % 16) != 0) return PA_ERR_WORKSPACE;
+  const int64_t parts = max_parts_for(max_context_len);
+  if ((int64_t)num_seqs * num_heads * parts > INT32_MAX) return PA_ERR_INVALID_ARG;
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.ws = static_cast<float*>(workspace);
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_rows = num_seqs;
+  a.num_seqs = num_seqs;
+  a.H = num_heads;
+  a.max_blocks = max_blocks_per_seq;
+  a.ws_parts = (int)parts + 1;
+  a.part_tiles = pa::kPartitionTokens / 16;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out_f32 = out_dtype == PA_F32 ? 1 : 0;
+  a.group_starts = group_starts;
+  a.prefix_lens = prefix_lens;
+  a.num_groups = num_groups;
+  const Dt dt = static_cast<Dt>(dtype);
+  hipError_t e = hipSuccess;
+  if (dtype != PA_F32 && max_prefix_len > 0) {
+    const int mpw = max_group_size <= 4 ? 4 : pa::kSharedMembersPerWave;
+    a.member_chunks = (int)ceil_div(max_group_size, mpw);
+    a.max_parts = (int)max_parts_for(max_prefix_len);
+    if ((int64_t)num_groups * a.member_chunks * num_heads * a.max_parts > INT32_MAX) return PA_ERR_INVALID_ARG;
+    e = pa::launch_decode_shared_prefix(a, dt, head_dim, block_size, mpw, stream);
+    a.max_parts = (int)parts;
+    if (e == hipSuccess) e = pa::launch_decode_partitions(a, dt, head_dim, block_size, pa::RowMode::SharedTail, stream);
+    if (e == hipSuccess) e = pa::launch_decode_reduce(a, dt, head_dim, true, stream);
+  } else {
+    // nothing shared to exploit (or f32): the ordinary split-K decode
+    a.max_parts = (int)parts;
+    e = pa::launch_decode_partitions(a, dt, head_dim, block_size, pa::RowMode::Decode, stream);
+    if (e == hipSuccess) e = pa::launch_decode_reduce(a, dt, head_dim, false, stream);
+  }
   return hip_status(e);
 }
 
@@ -272,10 +345,11 @@ pa_status pa_paged_attention_prefill(void* out, pa_dtype out_dtype, const void* 
   a.H = num_heads;
   a.max_blocks = max_blocks_per_seq;
   a.max_parts = 1;
+  a.ws_parts = 1;
   a.part_tiles = (int)std::max<int64_t>(1, ceil_div(max_context_len, 16));
   a.scale_log2 = scale_log2;
   a.out_f32 = 1;
-  return hip_status(pa::launch_decode_partitions(a, Dt::F32, head_dim, block_size, true, stream));
+  return hip_status(pa::launch_decode_partitions(a, Dt::F32, head_dim, block_size, pa::RowMode::PrefillRows, stream));
 }
 
 }  // extern "C"

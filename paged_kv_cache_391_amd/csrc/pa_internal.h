@@ -26,6 +26,13 @@ constexpr int kDecodeHeadsPerGroup = PA_DECODE_HEADS;
 constexpr int kPartitionTokens = PA_PARTITION_TOKENS;
 static_assert(kPartitionTokens % 32 == 0, "partitions must hold whole 16- and 32-token blocks");
 
+// Which rows a partition-kernel launch walks.
+enum class RowMode : int {
+  Decode = 0,       // row s = sequence s, tokens [0, ctx)
+  PrefillRows = 1,  // row r = one query of a causal chunk, tokens [0, its position]
+  SharedTail = 2,   // row s = sequence s of a prefix-sharing group, tokens [prefix, ctx)
+};
+
 struct DecodeArgs {
   void* out;                        // [rows][H][D], fp32 or the input dtype
   float* ws;                        // split-K partials (nullptr: single partition)
@@ -40,7 +47,12 @@ struct DecodeArgs {
   int H;
   int max_blocks;
   int max_parts;                    // partitions per row in the grid
+  int ws_parts;                     // partition slots per (row, head) in the workspace
   int part_tiles;                   // 16-token tiles per partition
+  const int32_t* group_starts;      // SharedTail / shared-prefix kernel: [num_groups+1] row ranges
+  const int32_t* prefix_lens;       // [num_groups] shared tokens (whole 16-token tiles)
+  int num_groups;
+  int member_chunks;                // shared-prefix kernel: waves per (group, head, partition)
   float scale_log2;                 // scale * log2(e)
   int out_f32;
 };
@@ -55,11 +67,17 @@ hipError_t launch_gather_kv(void* k_out, void* v_out, const void* k_cache, const
                             int S, int max_ctx, int H, int D, int BS, int max_blocks, int elt_bytes,
                             hipStream_t stream);
 
-// partition kernel (K2); prefill_rows selects the per-query-row mode
-hipError_t launch_decode_partitions(const DecodeArgs& a, Dt dt, int D, int BS, bool prefill_rows,
-                                    hipStream_t stream);
-// reduction kernel (K3)
-hipError_t launch_decode_reduce(const DecodeArgs& a, Dt dt, int D, hipStream_t stream);
+// partition kernel (K2) over the rows `mode` describes
+hipError_t launch_decode_partitions(const DecodeArgs& a, Dt dt, int D, int BS, RowMode mode, hipStream_t stream);
+// reduction kernel (K3); shared = rows carry a shared-prefix partition offset
+hipError_t launch_decode_reduce(const DecodeArgs& a, Dt dt, int D, bool shared, hipStream_t stream);
+// shared-prefix partitions: each shared K/V tile read once per group (f16/bf16)
+hipError_t launch_decode_shared_prefix(const DecodeArgs& a, Dt dt, int D, int BS, int members_per_wave,
+                                       hipStream_t stream);
+#ifndef PA_SHARED_MEMBERS
+#define PA_SHARED_MEMBERS 8
+#endif
+constexpr int kSharedMembersPerWave = PA_SHARED_MEMBERS;  // 4 or 8: members one wave scores (groups > 4)
 
 // MFMA causal prefill (K4), fp16/bf16 only
 struct PrefillArgs {

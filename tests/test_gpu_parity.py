@@ -250,6 +250,104 @@ def test_decode_bit_identical_with_aliased_or_private_prefix_blocks():
     assert np.abs(base.astype(np.float64) - ref).max() <= ATOL["f16"]
 
 
+# ------------------------------------------------- shared-prefix decode
+
+def _groups_for_prefix_workload(wl):
+    """Group metadata of the prefix-sharing workload: consecutive rows of one
+    prompt, sharing the prompt's whole blocks."""
+    notes = wl.notes
+    samples = len(notes["tails"][0])
+    plens = notes["prompt_lens"]
+    gs = np.arange(0, samples * len(plens) + 1, samples, dtype=np.int32)
+    pl = np.array([(p // wl.block_size) * wl.block_size for p in plens], dtype=np.int32)
+    return gs, pl, samples
+
+
+def _shared_decode(od, wl, gs, pl, max_group, out_dtype=torch.float32):
+    d = wl.decode
+    out = torch.empty(od.q.shape, dtype=out_dtype, device="cuda")
+    ws = pa.make_decode_shared_workspace(d.num_seqs, wl.num_heads, wl.head_dim, d.max_context_len)
+    pa.paged_attention_decode_shared_prefix(out, od.q, od.k_cache, od.v_cache, od.block_tables, od.context_lens,
+                                            dev(gs), dev(pl), wl.scale, d.max_context_len, max_group,
+                                            int(pl.max()), ws)
+    return out
+
+
+@pytest.mark.parametrize("cow", [False, True])
+def test_shared_prefix_decode_prefix_workload(cow):
+    wl = config4(cow=True) if cow else _config(4)[0]
+    if cow:
+        kc_ref, vc_ref = oracle.reshape_and_cache(wl.new.k, wl.new.v, wl.k_cache, wl.v_cache, wl.new.slot_mapping,
+                                                  wl.block_size, wl.dtype)
+    else:
+        _, kc_ref, vc_ref = _config(4)
+    od = _on_device_written(wl)
+    gs, pl, samples = _groups_for_prefix_workload(wl)
+    d = wl.decode
+    ref = oracle.decode(d.q, kc_ref, vc_ref, d.block_tables, d.context_lens, wl.scale, wl.dtype)
+    out = _shared_decode(od, wl, gs, pl, samples)
+    err = _check_attention(out, ref, wl.dtype)
+    plain = host(od.decode(torch.float32)).astype(np.float64)
+    assert np.abs(host(out).astype(np.float64) - plain).max() <= ATOL[wl.dtype]
+    outn = _shared_decode(od, wl, gs, pl, samples, TORCH_DT[wl.dtype])
+    assert np.array_equal(bits(host(outn)), bits(rne(host(out), wl.dtype)))
+    print(f"shared-prefix decode ({'cow' if cow else 'aligned'}) max abs err {err:.2e}")
+
+
+def _grouped_batch(dtype, bs, groups, seed):
+    """groups: list of (members, prefix_tokens, [tail tokens per member]).
+    Blocks come from the library's allocator (fork shares the prefix)."""
+    from workloads import normal
+    rng = np.random.default_rng(seed)
+    H, D = 4, 128
+    need = sum(-(-p // bs) + sum(-(-t // bs) + 1 for t in tails) for _, p, tails in groups) + 8
+    alloc = pa.BlockAllocator(need, bs)
+    rows, gs, pl = [], [0], []
+    for members, prefix, tails in groups:
+        assert members == len(tails) and prefix % bs == 0
+        first = alloc.new_sequence()
+        alloc.append(first, prefix)
+        seqs = [first] + [alloc.fork(first) for _ in range(members - 1)]
+        for sq, t in zip(seqs, tails):
+            alloc.append(sq, t)
+        rows += seqs
+        gs.append(gs[-1] + members)
+        pl.append(prefix)
+    assert alloc.take_copies().shape[0] == 0  # whole-block prefixes: nothing copied
+    tables = [alloc.block_table(r) for r in rows]
+    ctx = np.array([alloc.length(r) for r in rows], dtype=np.int32)
+    maxb = max(1, max(t.size for t in tables))
+    bt = np.full((len(rows), maxb), -1, dtype=np.int32)
+    for i, t in enumerate(tables):
+        bt[i, :t.size] = t
+    kc = normal(rng, (need, H, bs, D), dtype)
+    vc = normal(rng, (need, H, bs, D), dtype)
+    q = normal(rng, (len(rows), H, D), dtype)
+    return kc, vc, q, bt, ctx, np.array(gs, dtype=np.int32), np.array(pl, dtype=np.int32)
+
+
+@pytest.mark.parametrize("dtype,bs", [("f16", 16), ("bf16", 32), ("f16", 32), ("f32", 16)])
+def test_shared_prefix_decode_ragged_groups(dtype, bs):
+    groups = [(1, 0, [37]), (3, bs, [0, 5, 700]), (8, 512, [0] * 4 + [1, 16, 300, 513]),
+              (11, 1056 if bs == 16 else 1024, [int(x) for x in np.arange(11) * 37]), (2, 512, [0, 0]),
+              (5, 0, [1, 2, 3, 600, 1200])]
+    kc, vc, q, bt, ctx, gs, pl = _grouped_batch(dtype, bs, groups, 31 + bs)
+    H, D = q.shape[1], q.shape[2]
+    scale = 1 / math.sqrt(D)
+    ref = oracle.decode(q, kc, vc, bt, ctx, scale, dtype)
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    maxctx = int(ctx.max())
+    ws = pa.make_decode_shared_workspace(len(ctx), H, D, maxctx)
+    dq, dk, dv = dev(q, dtype), dev(kc, dtype), dev(vc, dtype)
+    pa.paged_attention_decode_shared_prefix(out, dq, dk, dv, dev(bt), dev(ctx), dev(gs), dev(pl), scale, maxctx,
+                                            int(np.diff(gs).max()), int(pl.max()), ws)
+    _check_attention(out, ref, dtype)
+    again = torch.empty_like(out)
+    pa.paged_attention_decode_shared_prefix(again, dq, dk, dv, dev(bt), dev(ctx), dev(gs), dev(pl), scale, maxctx,
+                                            int(np.diff(gs).max()), int(pl.max()), ws)
+    assert torch.equal(out, again)
+
+
 # ----------------------------------------------------------------- prefill
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
