@@ -219,9 +219,9 @@ pa_status pa_paged_attention_decode_reduce(void* out, pa_dtype out_dtype, const 
  * and FAQ answer on parallel sampling; devpress page, "实际收益远超预期").
  * Computes exactly what pa_paged_attention_decode computes, but reads each
  * shared K/V tile once per group instead of once per sequence: one wave
- * scores the queries of up to 8 group members against every shared tile,
- * each member's private tail runs as ordinary split-K partitions, and the
- * reduction merges both.
+ * scores the queries of up to 16 group members against every shared tile
+ * on the matrix cores, each member's private tail runs as ordinary split-K
+ * partitions, and the reduction merges both.
  *   group_starts  int32 [num_groups+1], device: rows group_starts[g] ..
  *                 group_starts[g+1]-1 form group g; group_starts[0] == 0,
  *                 non-decreasing, group_starts[num_groups] == num_seqs

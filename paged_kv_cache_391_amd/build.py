@@ -6,7 +6,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpagedattn.so")
-SOURCES = ["pa_api.hip", "pa_cache.hip", "pa_decode.hip", "pa_prefill.hip", "pa_alloc.cpp"]
+SOURCES = ["pa_api.hip", "pa_cache.hip", "pa_decode.hip", "pa_prefill.hip", "pa_shared.hip", "pa_alloc.cpp"]
 ARCH = "gfx950"
 
 

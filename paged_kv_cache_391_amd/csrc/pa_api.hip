@@ -271,11 +271,10 @@ pa_status pa_paged_attention_decode_shared_prefix(
   const Dt dt = static_cast<Dt>(dtype);
   hipError_t e = hipSuccess;
   if (dtype != PA_F32 && max_prefix_len > 0) {
-    const int mpw = max_group_size <= 4 ? 4 : pa::kSharedMembersPerWave;
-    a.member_chunks = (int)ceil_div(max_group_size, mpw);
+    a.member_chunks = (int)ceil_div(max_group_size, pa::kSharedMembersPerWave);
     a.max_parts = (int)max_parts_for(max_prefix_len);
     if ((int64_t)num_groups * a.member_chunks * num_heads * a.max_parts > INT32_MAX) return PA_ERR_INVALID_ARG;
-    e = pa::launch_decode_shared_prefix(a, dt, head_dim, block_size, mpw, stream);
+    e = pa::launch_shared_prefix_mfma(a, dt, head_dim, block_size, stream);
     a.max_parts = (int)parts;
     if (e == hipSuccess) e = pa::launch_decode_partitions(a, dt, head_dim, block_size, pa::RowMode::SharedTail, stream);
     if (e == hipSuccess) e = pa::launch_decode_reduce(a, dt, head_dim, true, stream);

@@ -386,221 +386,6 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(const DecodeArgs a) {
   for (int i = 0; i < PER; ++i) store_out<DT>(a.out, orow + lane + 64 * i, x[i] / Lsum, a.out_f32);
 }
 
-// Shared-prefix partitions. Parallel samples of one prompt list the same
-// physical blocks for the prompt (aidocs.cortexgrid.cn page, FAQ answer on
-// parallel sampling; devpress.csdn.net page, "实际收益远超预期"), so one
-// wave streams each shared K/V tile once and scores the queries of up to MC
-// samples against it, instead of every sample re-reading the prompt. Same
-// lane mapping as the partition kernel (a 16-lane row holds one token row);
-// each lane keeps every member's q slice and, per 16-lane row and member, an
-// online-softmax state. The shared prefix is whole 16-token tiles, so no
-// tile needs a mask. The running max is raised lazily (only when a tile's
-// max exceeds it by more than 2^8, wave-uniform), so accumulators are
-// rescaled on few tiles. Grid: partition-major, then group, member chunk
-// and head group; the member chunks of one (group, partition, head) are
-// neighbours, so extra chunks hit the tile in L2.
-constexpr float kSharedRescaleLog2 = 8.f;
-
-template <Dt DT, int D, int BS, int HG, int MC>
-__global__ __launch_bounds__(HG * 64, MC > 4 ? 1 : 2) void decode_shared_prefix_kernel(const DecodeArgs a) {
-  using L = Lane<DT, D>;
-  constexpr int WPL = L::WPL;
-  constexpr int EPL = L::EPL;
-  constexpr int TPB = BS / 16;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 4;
-  const int c = lane & 15;
-
-  const int n_hg = (a.H + HG - 1) / HG;
-  int bid = blockIdx.x;
-  const int hg = bid % n_hg;
-  bid /= n_hg;
-  const int mc = bid % a.member_chunks;
-  bid /= a.member_chunks;
-  const int grp = bid % a.num_groups;
-  const int part = bid / a.num_groups;
-  const int h = hg * HG + wave;
-  if (h >= a.H) return;
-
-  const int r_begin = a.group_starts[grp];
-  const int m0 = r_begin + mc * MC;
-  const int nm = min(MC, a.group_starts[grp + 1] - m0);
-  if (nm <= 0) return;
-  const int pt = a.part_tiles * 16;
-  const int prefix = min(a.prefix_lens[grp], a.context_lens[r_begin]) & ~15;  // whole tiles of the first member
-  const int ns = (prefix + pt - 1) / pt;
-  if (part >= ns) return;
-  const int u0 = part * a.part_tiles;
-  const int my_tiles = min(prefix >> 4, u0 + a.part_tiles) - u0;
-
-  uint32_t qw[MC][WPL];
-#pragma unroll
-  for (int m = 0; m < MC; ++m) {
-    if (m < nm) {
-      L::load(qw[m], reinterpret_cast<const char*>(a.q) + ((int64_t)(m0 + m) * a.H + h) * L::ROW_BYTES,
-              (uint32_t)(c * L::VB));
-    } else {
-#pragma unroll
-      for (int i = 0; i < WPL; ++i) qw[m][i] = 0u;
-    }
-  }
-  float mrow[MC], lrow[MC], acc[MC][EPL];
-#pragma unroll
-  for (int m = 0; m < MC; ++m) {
-    mrow[m] = -INFINITY;
-    lrow[m] = 0.f;
-#pragma unroll
-    for (int k = 0; k < EPL; ++k) acc[m][k] = 0.f;
-  }
-
-  const int32_t* bt_row = a.block_tables + (int64_t)r_begin * a.max_blocks;  // members share these entries
-  const char* kc = reinterpret_cast<const char*>(a.k_cache);
-  const char* vc = reinterpret_cast<const char*>(a.v_cache);
-  const uint32_t lane_off = (uint32_t)(g * L::ROW_BYTES + c * L::VB);
-
-  // token 4*j + g of a tile is in kw[j]/vw[j]; every token is valid
-  auto consume = [&](const uint32_t (&kw)[4][WPL], const uint32_t (&vw)[4][WPL]) {
-    float sc[MC][4];
-    bool grow = false;
-#pragma unroll
-    for (int m = 0; m < MC; ++m) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sc[m][j] = row16_sum(L::dot(qw[m], kw[j])) * a.scale_log2;
-      const float mt = fmaxf(fmaxf(sc[m][0], sc[m][1]), fmaxf(sc[m][2], sc[m][3]));
-      grow |= mt > mrow[m] + kSharedRescaleLog2;
-    }
-    if (__any(grow)) {
-#pragma unroll
-      for (int m = 0; m < MC; ++m) {
-        const float mt = fmaxf(fmaxf(sc[m][0], sc[m][1]), fmaxf(sc[m][2], sc[m][3]));
-        if (mt > mrow[m] + kSharedRescaleLog2) {
-          const float alpha = fast_exp2(mrow[m] - mt);
-          lrow[m] *= alpha;
-#pragma unroll
-          for (int k = 0; k < EPL; ++k) acc[m][k] *= alpha;
-          mrow[m] = mt;
-        }
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < MC; ++m) {
-      float pj[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) pj[j] = fast_exp2(sc[m][j] - mrow[m]);
-      lrow[m] += (pj[0] + pj[1]) + (pj[2] + pj[3]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) L::axpy(acc[m], pj[j], vw[j]);
-    }
-  };
-
-  for (int base = 0; base < my_tiles; base += 64) {
-    const int cnt = min(64, my_tiles - base);
-    int32_t tb = 0;
-    if (lane < cnt) tb = bt_row[(u0 + base + lane) / TPB];
-    auto tile_off = [&](int i) -> int64_t {
-      const int u = u0 + base + i;
-      const int32_t phys = __builtin_amdgcn_readlane(tb, i);
-      return kv_row_offset(phys, h, (u % TPB) * 16, a.H, BS, D) * L::EB;
-    };
-    auto load_tile = [&](uint32_t (&kw)[4][WPL], uint32_t (&vw)[4][WPL], int64_t off) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) L::template load<true>(kw[j], kc + off + j * 4 * L::ROW_BYTES, lane_off);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) L::template load<true>(vw[j], vc + off + j * 4 * L::ROW_BYTES, lane_off);
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    uint32_t ka[4][WPL], va[4][WPL], kb[4][WPL], vb[4][WPL];
-    load_tile(ka, va, tile_off(0));
-    int i = 0;
-    for (; i + 2 < cnt; i += 2) {
-      load_tile(kb, vb, tile_off(i + 1));
-      consume(ka, va);
-      load_tile(ka, va, tile_off(i + 2));
-      consume(kb, vb);
-    }
-    if (i + 1 < cnt) {
-      load_tile(kb, vb, tile_off(i + 1));
-      consume(ka, va);
-      consume(kb, vb);
-    } else {
-      consume(ka, va);
-    }
-  }
-
-  // per member: merge the four 16-lane rows, then write the partial (or the
-  // output when this is the row's only partition)
-#pragma unroll
-  for (int m = 0; m < MC; ++m) {
-    if (m >= nm) break;
-    float m_all = fmaxf(mrow[m], shfl_xor_f(mrow[m], 16));
-    m_all = fmaxf(m_all, shfl_xor_f(m_all, 32));
-    const float f = fast_exp2(mrow[m] - m_all);
-    float lw = lrow[m] * f;
-    lw += shfl_xor_f(lw, 16);
-    lw += shfl_xor_f(lw, 32);
-    float o[EPL];
-#pragma unroll
-    for (int k = 0; k < EPL; ++k) {
-      float x = acc[m][k] * f;
-      x += shfl_xor_f(x, 16);
-      x += shfl_xor_f(x, 32);
-      o[k] = x;
-    }
-    if (g != 0) continue;
-    const int row = m0 + m;
-    const int ctx = a.context_lens[row];
-    const int own_tiles = ((ctx + 15) >> 4) - (prefix >> 4);
-    const int total = ns + (own_tiles + a.part_tiles - 1) / a.part_tiles;
-    if (total <= 1) {
-      const int64_t orow = ((int64_t)row * a.H + h) * D;
-#pragma unroll
-      for (int k = 0; k < EPL; ++k) store_out<DT>(a.out, orow + L::elem(c, k), o[k] / lw, a.out_f32);
-    } else {
-      const int64_t prow = ((int64_t)row * a.H + h) * a.ws_parts + part;
-      float* acc_out = a.ws + prow * D;
-#pragma unroll
-      for (int k = 0; k < EPL; ++k) acc_out[L::elem(c, k)] = o[k];
-      if (c == 0) {
-        float* ml = a.ws + (int64_t)a.num_rows * a.H * a.ws_parts * D + prow * 2;
-        ml[0] = m_all;
-        ml[1] = lw;
-      }
-    }
-  }
-}
-
-template <Dt DT, int D, int BS, int MC>
-static hipError_t launch_shared(const DecodeArgs& a, hipStream_t stream) {
-  const int64_t n_hg = (a.H + kDecodeHeadsPerGroup - 1) / kDecodeHeadsPerGroup;
-  const int64_t grid = (int64_t)a.num_groups * a.member_chunks * n_hg * a.max_parts;
-  if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((decode_shared_prefix_kernel<DT, D, BS, kDecodeHeadsPerGroup, MC>), dim3((unsigned)grid),
-                     dim3(kDecodeHeadsPerGroup * 64), 0, stream, a);
-  return hipGetLastError();
-}
-
-template <Dt DT, int MC>
-static hipError_t dispatch_shared(const DecodeArgs& a, int D, int BS, hipStream_t stream) {
-  if (D == 128 && BS == 16) return launch_shared<DT, 128, 16, MC>(a, stream);
-  if (D == 128 && BS == 32) return launch_shared<DT, 128, 32, MC>(a, stream);
-  if (D == 64 && BS == 16) return launch_shared<DT, 64, 16, MC>(a, stream);
-  if (D == 64 && BS == 32) return launch_shared<DT, 64, 32, MC>(a, stream);
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_decode_shared_prefix(const DecodeArgs& a, Dt dt, int D, int BS, int members_per_wave,
-                                       hipStream_t stream) {
-  if (dt == Dt::F16)
-    return members_per_wave <= 4 ? dispatch_shared<Dt::F16, 4>(a, D, BS, stream)
-                                 : dispatch_shared<Dt::F16, 8>(a, D, BS, stream);
-  if (dt == Dt::BF16)
-    return members_per_wave <= 4 ? dispatch_shared<Dt::BF16, 4>(a, D, BS, stream)
-                                 : dispatch_shared<Dt::BF16, 8>(a, D, BS, stream);
-  return hipErrorInvalidValue;
-}
-
 template <Dt DT, int D, int BS, RowMode MODE>
 static hipError_t launch_k2(const DecodeArgs& a, hipStream_t stream) {
   const int64_t n_hg = (a.H + kDecodeHeadsPerGroup - 1) / kDecodeHeadsPerGroup;

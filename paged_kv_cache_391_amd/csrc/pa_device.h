@@ -54,6 +54,35 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
   return u >> 16;
 }
 
+// ---- matrix cores ------------------------------------------------------------
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// D = A B + C on v_mfma_f32_16x16x32_{f16,bf16}: A 16x32 (lane l holds row
+// l%16, k = 8*(l/16)..+7), B 32x16 (lane l holds column l%16, the same 8 k),
+// C/D 16x16 fp32 (lane l holds rows 4*(l/16)..+3 of column l%16).
+template <Dt DT> __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (DT == Dt::F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// 16-bit bits of x in the input type (round to nearest even), and back
+template <Dt DT> __device__ __forceinline__ uint32_t to_bits(float x) {
+  if constexpr (DT == Dt::F16) return f32_to_f16_bits(x);
+  else return f32_to_bf16_bits(x);
+}
+template <Dt DT> __device__ __forceinline__ float from_bits(uint32_t b) {
+  if constexpr (DT == Dt::F16) return f16_bits_to_f32(b);
+  else return bf16_bits_to_f32(b);
+}
+
 // ---- paged address translation ---------------------------------------------
 // Caches are [num_blocks][H][BS][D]. Logical token t of a sequence lives in
 // physical block table[t / BS] at offset t % BS; one (block, head) tile of

@@ -71,13 +71,10 @@ hipError_t launch_gather_kv(void* k_out, void* v_out, const void* k_cache, const
 hipError_t launch_decode_partitions(const DecodeArgs& a, Dt dt, int D, int BS, RowMode mode, hipStream_t stream);
 // reduction kernel (K3); shared = rows carry a shared-prefix partition offset
 hipError_t launch_decode_reduce(const DecodeArgs& a, Dt dt, int D, bool shared, hipStream_t stream);
-// shared-prefix partitions: each shared K/V tile read once per group (f16/bf16)
-hipError_t launch_decode_shared_prefix(const DecodeArgs& a, Dt dt, int D, int BS, int members_per_wave,
-                                       hipStream_t stream);
-#ifndef PA_SHARED_MEMBERS
-#define PA_SHARED_MEMBERS 8
-#endif
-constexpr int kSharedMembersPerWave = PA_SHARED_MEMBERS;  // 4 or 8: members one wave scores (groups > 4)
+// shared-prefix partitions on the matrix cores: each shared K/V tile is read
+// once per group, one wave per 16 members (f16/bf16)
+hipError_t launch_shared_prefix_mfma(const DecodeArgs& a, Dt dt, int D, int BS, hipStream_t stream);
+constexpr int kSharedMembersPerWave = 16;
 
 // MFMA causal prefill (K4), fp16/bf16 only
 struct PrefillArgs {

@@ -34,10 +34,6 @@ namespace pa {
 
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
 #ifndef PA_PREFILL_KT
 #define PA_PREFILL_KT 32
 #endif
@@ -51,27 +47,6 @@ constexpr int QT = 4 * QW;         // queries per workgroup
 constexpr int MAXB_LDS = 256;      // block-table entries staged in LDS (a sliding window)
 constexpr float RESCALE_LOG2 = 8.f; // lazy rescale threshold (log2 units): p < 256 between rescales
 static_assert(KT == 32 || KT == 64, "key tile must be 32 or 64");
-
-template <Dt DT> __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
-  if constexpr (DT == Dt::F16)
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
-                                                  0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
-                                                   0, 0, 0);
-}
-
-// 16-bit bits of x in the input type (round to nearest even)
-template <Dt DT> __device__ __forceinline__ uint32_t to_bits(float x) {
-  if constexpr (DT == Dt::F16) return f32_to_f16_bits(x);
-  else return f32_to_bf16_bits(x);
-}
-template <Dt DT> __device__ __forceinline__ float from_bits(uint32_t b) {
-  if constexpr (DT == Dt::F16) return f16_bits_to_f32(b);
-  else return bf16_bits_to_f32(b);
-}
-
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 }  // namespace
 
@@ -238,7 +213,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
       for (int ks = 0; ks < KS; ++ks) {
         const u32x4 ka = *reinterpret_cast<const u32x4*>(&sk[b][(sub * 16 + n16) * KROW + ks * 32 + 8 * g4]);
 #pragma unroll
-        for (int g = 0; g < NQ; ++g) sacc[g][sub] = mfma<DT>(ka, qf[g][ks], sacc[g][sub]);
+        for (int g = 0; g < NQ; ++g) sacc[g][sub] = mfma16<DT>(ka, qf[g][ks], sacc[g][sub]);
       }
     }
     // online softmax; lane holds query n16, keys kv0 + 16*sub + 4*g4 + i.
@@ -310,8 +285,8 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
         const u32x4 va = u32x4{lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
         for (int g = 0; g < NQ; ++g) {
-          o[g][dt] = mfma<DT>(va, pb[g][kst], o[g][dt]);
-          if constexpr (DT == Dt::BF16) o[g][dt] = mfma<DT>(va, pbl[g][kst], o[g][dt]);
+          o[g][dt] = mfma16<DT>(va, pb[g][kst], o[g][dt]);
+          if constexpr (DT == Dt::BF16) o[g][dt] = mfma16<DT>(va, pbl[g][kst], o[g][dt]);
         }
       }
     }
