@@ -22,7 +22,9 @@ One step = the workload's whole path, all inputs resident in HBM:
 reshape_and_cache of the step's new tokens, [prefill,] then split-K decode
 (partition kernel + reduction kernel) with an output in the input dtype.
 The timed steps replay the step captured as a HIP graph (checked
-bit-identical to the eager step); --eager times plain launches instead.
+bit-identical to the eager step); --eager times plain launches instead. The
+mixed step is timed as one pa_attention_step call with the prefill on a
+side stream next to the decode (the in-order graph is timed too).
 
 Prints ONE JSON line: value = algorithmic bytes of the step / step time
 (GB/s, 1e9 B/s); roofline = the decode partition kernel's algorithmic bytes
@@ -309,39 +311,63 @@ def main():
     eager_out = out.clone()
     eager_pf = pf_out.clone() if pf_out is not None else None
 
-    # timed pass: the step captured once as a HIP graph and replayed, as a
-    # serving loop runs it (no host launch gaps between the kernels)
-    ms_per_step = eager_ms
-    graph_ok = None
-    if not args.eager:
+    # the mixed step as one scheduler iteration: pa_attention_step with the
+    # prefill on a side stream, concurrent with the decode
+    step_side = torch.cuda.Stream() if p is not None else None
+    step_events = pa.make_step_events() if p is not None else None
+
+    def concurrent_step():
+        pa.attention_step(od.k_cache, od.v_cache, wl.scale, od.new_k, od.new_v, od.slot_mapping,
+                          prefill_out=pf_out, prefill_q=od.pf_q, prefill_block_tables=od.pf_block_tables,
+                          prefill_context_lens=od.pf_context_lens, prefill_query_start_loc=od.pf_qsl,
+                          prefill_max_q_len=p.max_q_len, prefill_max_context_len=p.max_context_len,
+                          decode_out=out, decode_q=od.q, decode_block_tables=od.block_tables,
+                          decode_context_lens=od.context_lens, decode_max_context_len=maxctx, workspace=ws,
+                          side_stream=step_side, fork_event=step_events[0], join_event=step_events[1])
+
+    def same():
+        ok = bool(torch.equal(out, eager_out))
+        return ok and (pf_out is None or bool(torch.equal(pf_out, eager_pf)))
+
+    def time_graph(fn):
+        """Capture fn once as a HIP graph; check replays against the eager
+        outputs; mean wall time per replay over args.steps back-to-back."""
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            step()
+            fn()
         torch.cuda.current_stream().wait_stream(side)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            step()
-
-        def same():
-            ok = bool(torch.equal(out, eager_out))
-            return ok and (pf_out is None or bool(torch.equal(pf_out, eager_pf)))
-
-        graph_ok = True
+            fn()
+        ok = True
         for _ in range(max(1, args.warmup)):
             out.zero_()
             if pf_out is not None:
                 pf_out.zero_()
             graph.replay()
             torch.cuda.synchronize()
-            graph_ok = graph_ok and same()
+            ok = ok and same()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(args.steps):
             graph.replay()
         torch.cuda.synchronize()
-        ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
-        graph_ok = graph_ok and same()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        return ms, ok and same()
+
+    # timed pass: the step captured once as a HIP graph and replayed, as a
+    # serving loop runs it (no host launch gaps between the kernels)
+    ms_per_step = eager_ms
+    graph_ok = None
+    sequential_ms = None
+    if not args.eager:
+        if p is not None:
+            sequential_ms, seq_ok = time_graph(step)
+            ms_per_step, graph_ok = time_graph(concurrent_step)
+            graph_ok = graph_ok and seq_ok
+        else:
+            ms_per_step, graph_ok = time_graph(step)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     k2_gbps = k2_bytes / (k2_ms * 1e-3) / 1e9
     log(f"[bench] {ms_per_step * 1e3:.1f} us/step ({'graph' if not args.eager else 'eager'}; eager "
@@ -400,7 +426,8 @@ def main():
                      "kernel": ("shared-prefix decode call (shared, tail and reduction kernels)" if shared
                                 else f"decode_partition_kernel<{wl.dtype},{D},{bs}>"),
                      "bytes_per_launch": k2_bytes, "avg_launch_us": round(k2_ms * 1e3, 2)},
-        "timing": "hip_graph_replay" if not args.eager else "eager",
+        "timing": ("hip_graph_replay" + (" of pa_attention_step (prefill on a side stream, concurrent with the "
+                                          "decode)" if p is not None else "")) if not args.eager else "eager",
         "eager_ms_per_step": round(eager_ms, 5),
         "hbm_copy_probe_GBps": round(copy_gbps, 1),
         "step_bytes": step_bytes,
@@ -416,6 +443,8 @@ def main():
     if p is not None:
         pf_tflops = pf_flops / (pf_ms * 1e-3) / 1e12
         rec["phases_us"]["prefill"] = round(pf_ms * 1e3, 2)
+        if sequential_ms is not None:
+            rec["sequential_ms_per_step"] = round(sequential_ms, 5)
         rec["prefill"] = {"bound": "mfma", "flops": pf_flops, "achieved_TFLOPs": round(pf_tflops, 1),
                           "peak_TFLOPs": MFMA_PEAK_TFLOPS[wl.dtype],
                           "mfma_frac": round(pf_tflops / MFMA_PEAK_TFLOPS[wl.dtype], 4), "bytes": pf_bytes,

@@ -274,6 +274,63 @@ pa_status pa_paged_attention_prefill(void* out, pa_dtype out_dtype, const void* 
                                      int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                                      float scale, pa_dtype dtype, hipStream_t stream);
 
+/*
+ * attention_step -- one scheduler iteration as a single call: the pages'
+ * continuous batching re-forms the batch every iteration, so one step mixes
+ * prompts being prefilled and sequences being decoded under a per-step
+ * token budget (devpress page, sections on continuous batching and
+ * max_num_batched_tokens; aidocs page, static vs continuous batching
+ * table). The call writes the step's new tokens (pa_reshape_and_cache),
+ * then runs the causal prefill of the chunks and the split-K decode of the
+ * decoding sequences, all against the same cache.
+ *   num_new_tokens == 0, num_prefill_seqs == 0 or num_decode_seqs == 0
+ *   skips that part. Field meanings and layouts are those of the three
+ *   single calls; the caches, heads, head_dim, block size, dtype and scale
+ *   are shared. workspace is the decode's split-K workspace.
+ *   side_stream  NULL: everything is queued on stream in order. Otherwise
+ *                (a different stream on the same device, with fork_event
+ *                and join_event created by the caller) the prefill runs on
+ *                side_stream concurrently with the decode on stream: the
+ *                call records fork_event on stream after the cache write,
+ *                makes side_stream wait for it, and makes stream wait for
+ *                join_event recorded on side_stream after the prefill, so
+ *                on return all work is ordered before anything queued
+ *                later on stream. Safe inside stream capture (fork/join).
+ * Every part is validated before anything is queued; an error leaves the
+ * streams untouched. Errors: those of the three calls, and INVALID_ARG for
+ * a side stream equal to stream or missing events.
+ */
+typedef struct {
+  void* k_cache;
+  void* v_cache;
+  int32_t num_blocks, num_heads, head_dim, block_size;
+  pa_dtype dtype;
+  float scale;
+  const void* new_k; /* [num_new_tokens][H][D] */
+  const void* new_v;
+  const int32_t* slot_mapping;
+  int32_t num_new_tokens;
+  void* prefill_out; /* [prefill_total_q][H][D] */
+  pa_dtype prefill_out_dtype;
+  const void* prefill_q;
+  const int32_t* prefill_block_tables;
+  const int32_t* prefill_context_lens;
+  const int32_t* prefill_query_start_loc;
+  int32_t num_prefill_seqs, prefill_total_q, prefill_max_q_len, prefill_max_blocks_per_seq,
+      prefill_max_context_len;
+  void* decode_out; /* [num_decode_seqs][H][D] */
+  pa_dtype decode_out_dtype;
+  const void* decode_q;
+  const int32_t* decode_block_tables;
+  const int32_t* decode_context_lens;
+  int32_t num_decode_seqs, decode_max_blocks_per_seq, decode_max_context_len;
+  void* workspace;
+  size_t workspace_bytes;
+} pa_step_args;
+
+pa_status pa_attention_step(const pa_step_args* step, hipStream_t stream, hipStream_t side_stream,
+                            hipEvent_t fork_event, hipEvent_t join_event);
+
 #ifdef __cplusplus
 }
 #endif

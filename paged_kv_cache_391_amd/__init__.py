@@ -14,6 +14,8 @@ Calls mirror the C ABI in ``include/pagedattn.h``:
 * ``paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, ...)``
 * ``paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale, ...)``
 * ``gather_kv(...)``, ``decode_workspace_bytes(...)`` and the two decode stages.
+* ``attention_step(...)``: one scheduler iteration (cache write, prefill,
+  decode) in one call, the prefill optionally on a side stream.
 
 Caches are ``[num_blocks, num_heads, block_size, head_dim]``; block tables
 ``int32 [num_seqs, max_blocks_per_seq]``; slots ``block * block_size + offset``.
@@ -31,6 +33,23 @@ PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = 0,
 PA_ERR_NO_BLOCKS, PA_ERR_NO_MEMORY = -5, -6
 _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 _lib = None
+
+_P, _I = ctypes.c_void_p, ctypes.c_int32
+
+
+class StepArgs(ctypes.Structure):
+    """Mirror of ``pa_step_args`` (C layout; checked against the header by
+    the tests)."""
+    _fields_ = [("k_cache", _P), ("v_cache", _P), ("num_blocks", _I), ("num_heads", _I), ("head_dim", _I),
+                ("block_size", _I), ("dtype", ctypes.c_int), ("scale", ctypes.c_float), ("new_k", _P),
+                ("new_v", _P), ("slot_mapping", _P), ("num_new_tokens", _I), ("prefill_out", _P),
+                ("prefill_out_dtype", ctypes.c_int), ("prefill_q", _P), ("prefill_block_tables", _P),
+                ("prefill_context_lens", _P), ("prefill_query_start_loc", _P), ("num_prefill_seqs", _I),
+                ("prefill_total_q", _I), ("prefill_max_q_len", _I), ("prefill_max_blocks_per_seq", _I),
+                ("prefill_max_context_len", _I), ("decode_out", _P), ("decode_out_dtype", ctypes.c_int),
+                ("decode_q", _P), ("decode_block_tables", _P), ("decode_context_lens", _P), ("num_decode_seqs", _I),
+                ("decode_max_blocks_per_seq", _I), ("decode_max_context_len", _I), ("workspace", _P),
+                ("workspace_bytes", ctypes.c_size_t)]
 
 
 class PagedAttnError(RuntimeError):
@@ -63,6 +82,8 @@ def lib():
         L.pa_paged_attention_prefill.argtypes = [P, ctypes.c_int, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F,
                                                  ctypes.c_int, P]
         L.pa_copy_blocks.argtypes = [P, P, P, I, I, I, I, I, ctypes.c_int, P]
+        L.pa_attention_step.argtypes = [ctypes.POINTER(StepArgs), P, P, P, P]
+        L.pa_attention_step.restype = ctypes.c_int
         L.pa_decode_shared_workspace_bytes.argtypes = [I, I, I, I]
         L.pa_decode_shared_workspace_bytes.restype = Z
         L.pa_paged_attention_decode_shared_prefix.argtypes = [P, ctypes.c_int, P, P, P, P, P, P, P, I, I, I, I, I, I,
@@ -326,6 +347,79 @@ def paged_attention_decode_reduce(out, context_lens, head_dim: int, max_context_
     _check("paged_attention_decode_reduce", lib().pa_paged_attention_decode_reduce(
         _ptr(out), _DT[out.dtype], _ptr(context_lens), int(context_lens.shape[0]), int(out.shape[1]),
         int(head_dim), int(max_context_len), _DT[in_dtype], _ptr(workspace), ws_bytes, _stream()))
+
+
+def make_step_events(n=2):
+    """Events for the fork/join of ``attention_step`` (created on the device:
+    a torch event gets its handle on its first record)."""
+    evs = [torch.cuda.Event() for _ in range(n)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    return evs
+
+
+def attention_step(k_cache, v_cache, scale: float, new_k=None, new_v=None, slot_mapping=None, prefill_out=None,
+                   prefill_q=None, prefill_block_tables=None, prefill_context_lens=None,
+                   prefill_query_start_loc=None, prefill_max_q_len=None, prefill_max_context_len=None,
+                   decode_out=None, decode_q=None, decode_block_tables=None, decode_context_lens=None,
+                   decode_max_context_len=None, workspace=None, side_stream=None, fork_event=None,
+                   join_event=None):
+    """One scheduler iteration: cache write of the new tokens, causal
+    prefill of the chunks and split-K decode, against the same cache. With
+    ``side_stream`` (and two events from ``make_step_events``) the prefill
+    runs on it concurrently with the decode on the current stream."""
+    nb, H, bs, D = _cache_dims(k_cache, v_cache)
+    a = StepArgs()
+    a.k_cache, a.v_cache = k_cache.data_ptr(), v_cache.data_ptr()
+    a.num_blocks, a.num_heads, a.head_dim, a.block_size = nb, H, D, bs
+    a.dtype, a.scale = _DT[k_cache.dtype], float(scale)
+    _dev(k_cache, v_cache)
+    if slot_mapping is not None:
+        _dev(new_k, new_v, slot_mapping)
+        _i32(slot_mapping)
+        T = int(slot_mapping.shape[0])
+        if new_k.shape != (T, H, D) or new_v.shape != (T, H, D) or new_k.dtype != k_cache.dtype:
+            raise ValueError("new_k/new_v must be [num_tokens, num_heads, head_dim] in the cache dtype")
+        a.new_k, a.new_v, a.slot_mapping, a.num_new_tokens = new_k.data_ptr(), new_v.data_ptr(), \
+            slot_mapping.data_ptr(), T
+    if prefill_q is not None:
+        _dev(prefill_out, prefill_q, prefill_block_tables, prefill_context_lens, prefill_query_start_loc)
+        _i32(prefill_block_tables, prefill_context_lens, prefill_query_start_loc)
+        S = int(prefill_context_lens.shape[0])
+        TQ = int(prefill_q.shape[0])
+        if prefill_q.shape != (TQ, H, D) or prefill_out.shape != (TQ, H, D) or prefill_q.dtype != k_cache.dtype:
+            raise ValueError("prefill q/out must be [total_q, num_heads, head_dim]")
+        if prefill_query_start_loc.shape != (S + 1,):
+            raise ValueError("prefill_query_start_loc must be [num_seqs + 1]")
+        a.prefill_out, a.prefill_out_dtype, a.prefill_q = prefill_out.data_ptr(), _DT[prefill_out.dtype], \
+            prefill_q.data_ptr()
+        a.prefill_block_tables, a.prefill_context_lens = prefill_block_tables.data_ptr(), \
+            prefill_context_lens.data_ptr()
+        a.prefill_query_start_loc = prefill_query_start_loc.data_ptr()
+        a.num_prefill_seqs, a.prefill_total_q = S, TQ
+        a.prefill_max_q_len, a.prefill_max_context_len = int(prefill_max_q_len), int(prefill_max_context_len)
+        a.prefill_max_blocks_per_seq = int(prefill_block_tables.shape[1])
+    if decode_q is not None:
+        _dev(decode_out, decode_q, decode_block_tables, decode_context_lens, workspace)
+        _i32(decode_block_tables, decode_context_lens)
+        S = int(decode_context_lens.shape[0])
+        if decode_q.shape != (S, H, D) or decode_out.shape != (S, H, D) or decode_q.dtype != k_cache.dtype:
+            raise ValueError("decode q/out must be [num_seqs, num_heads, head_dim]")
+        a.decode_out, a.decode_out_dtype, a.decode_q = decode_out.data_ptr(), _DT[decode_out.dtype], \
+            decode_q.data_ptr()
+        a.decode_block_tables, a.decode_context_lens = decode_block_tables.data_ptr(), decode_context_lens.data_ptr()
+        a.num_decode_seqs, a.decode_max_context_len = S, int(decode_max_context_len)
+        a.decode_max_blocks_per_seq = int(decode_block_tables.shape[1])
+        if workspace is not None:
+            a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    side = ctypes.c_void_p(side_stream.cuda_stream) if side_stream is not None else ctypes.c_void_p(0)
+    if side_stream is not None and (fork_event is None or join_event is None or not fork_event.cuda_event
+                                    or not join_event.cuda_event):
+        raise ValueError("a side stream needs two created events (see make_step_events)")
+    fe = ctypes.c_void_p(fork_event.cuda_event if fork_event is not None else 0)
+    je = ctypes.c_void_p(join_event.cuda_event if join_event is not None else 0)
+    _check("attention_step", lib().pa_attention_step(ctypes.byref(a), _stream(), side, fe, je))
 
 
 def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale: float,

@@ -287,13 +287,23 @@ pa_status pa_paged_attention_decode_shared_prefix(
   return hip_status(e);
 }
 
-pa_status pa_paged_attention_prefill(void* out, pa_dtype out_dtype, const void* q, const void* k_cache,
-                                     const void* v_cache, const int32_t* block_tables,
-                                     const int32_t* context_lens, const int32_t* query_start_loc,
-                                     int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t num_heads,
-                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                                     int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
-                                     float scale, pa_dtype dtype, hipStream_t stream) {
+// Validated launch plan of one prefill call: the MFMA kernel (f16/bf16) or
+// the per-query-row vector path (f32).
+struct PrefillCall {
+  bool mfma = false;
+  bool empty = true;
+  pa::PrefillArgs pf{};
+  pa::DecodeArgs rows{};
+  Dt dt = Dt::F16;
+  int D = 0, BS = 0;
+};
+
+static pa_status prepare_prefill(PrefillCall& call, void* out, pa_dtype out_dtype, const void* q,
+                                 const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                                 const int32_t* context_lens, const int32_t* query_start_loc, int32_t num_seqs,
+                                 int32_t total_q, int32_t max_q_len, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                 int32_t max_blocks_per_seq, int32_t max_context_len, float scale, pa_dtype dtype) {
   pa_status st = check_cache_shape(num_heads, head_dim, block_size, num_blocks, dtype);
   if (st != PA_OK) return st;
   if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || max_blocks_per_seq <= 0 || max_context_len < 0)
@@ -304,12 +314,17 @@ pa_status pa_paged_attention_prefill(void* out, pa_dtype out_dtype, const void* 
   if (max_q_len > max_context_len || (num_seqs > 0 && total_q > (int64_t)num_seqs * max_q_len))
     return PA_ERR_INVALID_ARG;
   if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
-  if (num_seqs == 0 || total_q == 0) return PA_OK;
+  call.empty = num_seqs == 0 || total_q == 0;
+  if (call.empty) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc)
     return PA_ERR_INVALID_ARG;
   const float scale_log2 = scale * 1.4426950408889634f;
-  if (dtype != PA_F32) {
-    pa::PrefillArgs a{};
+  call.dt = static_cast<Dt>(dtype);
+  call.D = head_dim;
+  call.BS = block_size;
+  call.mfma = dtype != PA_F32;
+  if (call.mfma) {
+    pa::PrefillArgs& a = call.pf;
     a.out = out;
     a.q = q;
     a.k_cache = k_cache;
@@ -326,11 +341,11 @@ pa_status pa_paged_attention_prefill(void* out, pa_dtype out_dtype, const void* 
     a.scale_log2 = scale_log2;
     a.out_f32 = out_dtype == PA_F32 ? 1 : 0;
     if ((int64_t)a.q_tiles * num_heads * num_seqs > INT32_MAX) return PA_ERR_INVALID_ARG;
-    return hip_status(pa::launch_prefill_mfma(a, static_cast<Dt>(dtype), head_dim, block_size, stream));
+    return PA_OK;
   }
   // fp32: every query row is a decode over its own causal prefix
   if ((int64_t)total_q * num_heads > INT32_MAX) return PA_ERR_INVALID_ARG;
-  pa::DecodeArgs a{};
+  pa::DecodeArgs& a = call.rows;
   a.out = out;
   a.ws = nullptr;
   a.q = q;
@@ -348,7 +363,85 @@ pa_status pa_paged_attention_prefill(void* out, pa_dtype out_dtype, const void* 
   a.part_tiles = (int)std::max<int64_t>(1, ceil_div(max_context_len, 16));
   a.scale_log2 = scale_log2;
   a.out_f32 = 1;
-  return hip_status(pa::launch_decode_partitions(a, Dt::F32, head_dim, block_size, pa::RowMode::PrefillRows, stream));
+  return PA_OK;
+}
+
+static hipError_t launch_prefill(const PrefillCall& call, hipStream_t stream) {
+  if (call.empty) return hipSuccess;
+  if (call.mfma) return pa::launch_prefill_mfma(call.pf, call.dt, call.D, call.BS, stream);
+  return pa::launch_decode_partitions(call.rows, Dt::F32, call.D, call.BS, pa::RowMode::PrefillRows, stream);
+}
+
+pa_status pa_paged_attention_prefill(void* out, pa_dtype out_dtype, const void* q, const void* k_cache,
+                                     const void* v_cache, const int32_t* block_tables,
+                                     const int32_t* context_lens, const int32_t* query_start_loc,
+                                     int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t num_heads,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                     int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                                     float scale, pa_dtype dtype, hipStream_t stream) {
+  PrefillCall call;
+  pa_status st = prepare_prefill(call, out, out_dtype, q, k_cache, v_cache, block_tables, context_lens,
+                                 query_start_loc, num_seqs, total_q, max_q_len, num_heads, num_kv_heads, head_dim,
+                                 block_size, num_blocks, max_blocks_per_seq, max_context_len, scale, dtype);
+  if (st != PA_OK) return st;
+  return hip_status(launch_prefill(call, stream));
+}
+
+pa_status pa_attention_step(const pa_step_args* s, hipStream_t stream, hipStream_t side_stream,
+                            hipEvent_t fork_event, hipEvent_t join_event) {
+  if (!s) return PA_ERR_INVALID_ARG;
+  // validate every part before anything is launched
+  pa_status st = check_cache_shape(s->num_heads, s->head_dim, s->block_size, s->num_blocks, s->dtype);
+  if (st != PA_OK) return st;
+  if (s->num_new_tokens < 0 || s->num_prefill_seqs < 0 || s->num_decode_seqs < 0) return PA_ERR_INVALID_ARG;
+  if (s->num_new_tokens > 0 && (!s->new_k || !s->new_v || !s->k_cache || !s->v_cache || !s->slot_mapping))
+    return PA_ERR_INVALID_ARG;
+  PrefillCall pf;
+  if (s->num_prefill_seqs > 0) {
+    st = prepare_prefill(pf, s->prefill_out, s->prefill_out_dtype, s->prefill_q, s->k_cache, s->v_cache,
+                         s->prefill_block_tables, s->prefill_context_lens, s->prefill_query_start_loc,
+                         s->num_prefill_seqs, s->prefill_total_q, s->prefill_max_q_len, s->num_heads, s->num_heads,
+                         s->head_dim, s->block_size, s->num_blocks, s->prefill_max_blocks_per_seq,
+                         s->prefill_max_context_len, s->scale, s->dtype);
+    if (st != PA_OK) return st;
+  }
+  DecodeCall dc;
+  const bool decode = s->num_decode_seqs > 0;
+  if (decode) {
+    st = prepare_decode(dc, s->decode_out, s->decode_out_dtype, s->decode_q, s->k_cache, s->v_cache,
+                        s->decode_block_tables, s->decode_context_lens, s->num_decode_seqs, s->num_heads,
+                        s->num_heads, s->head_dim, s->block_size, s->num_blocks, s->decode_max_blocks_per_seq,
+                        s->decode_max_context_len, s->scale, s->dtype, s->workspace, s->workspace_bytes);
+    if (st != PA_OK) return st;
+  }
+  const bool prefill = !pf.empty;
+  const bool fork = prefill && decode && side_stream != nullptr;
+  if (fork && (side_stream == stream || !fork_event || !join_event)) return PA_ERR_INVALID_ARG;
+
+  hipError_t e = hipSuccess;
+  if (s->num_new_tokens > 0)
+    e = pa::launch_reshape_and_cache(s->new_k, s->new_v, s->k_cache, s->v_cache, s->slot_mapping, s->num_new_tokens,
+                                     s->num_heads, s->head_dim, s->block_size, s->num_blocks, elt_bytes(s->dtype),
+                                     stream);
+  if (e != hipSuccess) return hip_status(e);
+  if (fork) {
+    // the prefill runs on the side stream next to the decode: both only read
+    // the cache the write above produced
+    e = hipEventRecord(fork_event, stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side_stream, fork_event, 0);
+    if (e == hipSuccess) e = launch_prefill(pf, side_stream);
+    if (e == hipSuccess) e = pa::launch_decode_partitions(dc.args, dc.dt, dc.D, dc.BS, pa::RowMode::Decode, stream);
+    if (e == hipSuccess && dc.split) e = pa::launch_decode_reduce(dc.args, dc.dt, dc.D, false, stream);
+    if (e == hipSuccess) e = hipEventRecord(join_event, side_stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(stream, join_event, 0);
+    return hip_status(e);
+  }
+  if (prefill) e = launch_prefill(pf, stream);
+  if (e == hipSuccess && decode) {
+    e = pa::launch_decode_partitions(dc.args, dc.dt, dc.D, dc.BS, pa::RowMode::Decode, stream);
+    if (e == hipSuccess && dc.split) e = pa::launch_decode_reduce(dc.args, dc.dt, dc.D, false, stream);
+  }
+  return hip_status(e);
 }
 
 }  // extern "C"

@@ -136,3 +136,36 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(4, 2, 16, 64)
     with pytest.raises(ValueError):
         pa.reshape_and_cache(torch.zeros(1, 2, 64), torch.zeros(1, 2, 64), x, x, torch.zeros(1, dtype=torch.int32))
+
+
+def test_step_args_layout_matches_the_header(tmp_path):
+    """The Python mirror of pa_step_args has the C layout: every field offset
+    and the size, as a C++ compiler reports them from the header."""
+    import subprocess
+    fields = [f[0] for f in pa.StepArgs._fields_]
+    src = tmp_path / "layout.cpp"
+    src.write_text("#include <cstdio>\n#include <cstddef>\n#include \"pagedattn.h\"\nint main() {\n"
+                   + "".join(f'  std::printf("%zu\\n", offsetof(pa_step_args, {f}));\n' for f in fields)
+                   + '  std::printf("%zu\\n", sizeof(pa_step_args));\n  return 0;\n}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["g++", "-std=c++17", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", "/opt/rocm/include", str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    want = [getattr(pa.StepArgs, f).offset for f in fields] + [ctypes.sizeof(pa.StepArgs)]
+    assert got == want
+
+
+def test_attention_step_validation():
+    L = pa.lib()
+    assert L.pa_attention_step(None, NULL, NULL, NULL, NULL) == pa.PA_ERR_INVALID_ARG
+    a = pa.StepArgs()
+    a.num_blocks, a.num_heads, a.head_dim, a.block_size, a.dtype, a.scale = 8, 2, 128, 16, 1, 0.1
+    assert L.pa_attention_step(ctypes.byref(a), NULL, NULL, NULL, NULL) == pa.PA_OK  # nothing to do
+    a.head_dim = 96
+    assert L.pa_attention_step(ctypes.byref(a), NULL, NULL, NULL, NULL) == pa.PA_ERR_UNSUPPORTED
+    a.head_dim = 128
+    a.num_new_tokens = 4  # new tokens without pointers
+    assert L.pa_attention_step(ctypes.byref(a), NULL, NULL, NULL, NULL) == pa.PA_ERR_INVALID_ARG
+    a.num_new_tokens = 0
+    a.num_decode_seqs, a.decode_max_blocks_per_seq, a.decode_max_context_len = 2, 4, 100  # q/out missing
+    assert L.pa_attention_step(ctypes.byref(a), NULL, NULL, NULL, NULL) == pa.PA_ERR_INVALID_ARG

@@ -467,3 +467,55 @@ def test_mixed_step_graph_replays_match_eager():
         assert torch.equal(dout, dref), f"decode differs on replay {i}"
         assert torch.equal(pout, pref), f"prefill differs on replay {i}"
         assert torch.isfinite(extra).all()
+
+
+@pytest.mark.parametrize("side", [False, True])
+def test_attention_step_matches_the_separate_calls(side):
+    """One scheduler iteration in one call (cache write, prefill, decode),
+    in order on one stream or with the prefill on a side stream: outputs and
+    caches equal, bit for bit, those of the three separate calls; captured
+    as a graph (fork/join across the two streams), every replay too."""
+    wl, _, _ = _config(5)
+    d, p = wl.decode, wl.prefill
+    ref = OnDevice(wl)
+    ws = pa.make_decode_workspace(d.num_seqs, wl.num_heads, wl.head_dim, d.max_context_len)
+    ref.write_new_tokens()
+    pref = torch.empty_like(ref.pf_q)
+    dref = torch.empty_like(ref.q)
+    pa.paged_attention_prefill(pref, ref.pf_q, ref.k_cache, ref.v_cache, ref.pf_block_tables, ref.pf_context_lens,
+                               ref.pf_qsl, wl.scale, p.max_q_len, p.max_context_len)
+    pa.paged_attention_decode(dref, ref.q, ref.k_cache, ref.v_cache, ref.block_tables, ref.context_lens, wl.scale,
+                              d.max_context_len, ws)
+    torch.cuda.synchronize()
+
+    od = OnDevice(wl)
+    pout = torch.empty_like(od.pf_q)
+    dout = torch.empty_like(od.q)
+    ws2 = pa.make_decode_workspace(d.num_seqs, wl.num_heads, wl.head_dim, d.max_context_len)
+    side_stream = torch.cuda.Stream() if side else None
+    fe, je = pa.make_step_events() if side else (None, None)
+
+    def step():
+        pa.attention_step(od.k_cache, od.v_cache, wl.scale, od.new_k, od.new_v, od.slot_mapping,
+                          prefill_out=pout, prefill_q=od.pf_q, prefill_block_tables=od.pf_block_tables,
+                          prefill_context_lens=od.pf_context_lens, prefill_query_start_loc=od.pf_qsl,
+                          prefill_max_q_len=p.max_q_len, prefill_max_context_len=p.max_context_len,
+                          decode_out=dout, decode_q=od.q, decode_block_tables=od.block_tables,
+                          decode_context_lens=od.context_lens, decode_max_context_len=d.max_context_len,
+                          workspace=ws2, side_stream=side_stream, fork_event=fe, join_event=je)
+
+    step()
+    torch.cuda.synchronize()
+    assert torch.equal(pout, pref) and torch.equal(dout, dref)
+    # unused slots hold NaN poison: compare the caches' bits
+    assert np.array_equal(bits(host(od.k_cache)), bits(host(ref.k_cache)))
+    assert np.array_equal(bits(host(od.v_cache)), bits(host(ref.v_cache)))
+    g = _capture(step)
+    for i in range(3):
+        pout.zero_()
+        dout.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(pout, pref), f"prefill differs on replay {i}"
+        assert torch.equal(dout, dref), f"decode differs on replay {i}"
