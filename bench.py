@@ -207,6 +207,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--plain", action="store_true", help="prefix13b: ordinary decode instead of the shared-prefix call")
+    ap.add_argument("--block-size", type=int, default=None,
+                    help="llama7b: block size (8/16/32/64) for the block-size trade-off; default 16")
     ap.add_argument("--copy-probe-gib", type=float, default=1.0, help="size of the plain-copy bandwidth probe")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="store HBM bytes per launch from two rocprofv3 --pmc runs of this script and exit")
@@ -230,7 +232,12 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     t = time.time()
-    wl = {"llama7b": config2, "mixed256": config3, "prefix13b": config4, "mixed_step": config5}[args.workload]()
+    if args.block_size is not None and args.workload != "llama7b":
+        raise SystemExit("--block-size applies to the llama7b workload only")
+    if args.block_size is not None:
+        wl = config2(block_size=args.block_size)
+    else:
+        wl = {"llama7b": config2, "mixed256": config3, "prefix13b": config4, "mixed_step": config5}[args.workload]()
     log(f"[bench] {args.workload}: generated in {time.time() - t:.1f}s: {wl.num_blocks} blocks, "
         f"sum ctx {int(wl.decode.context_lens.sum())}")
     od = OnDevice(wl)
@@ -435,6 +442,11 @@ def main():
                       "decode_reduce": round(k3_ms * 1e3, 2)},
         "cpu_baseline": cpu,
     }
+    if args.block_size is not None:
+        used_slots = int((-(-d.context_lens.astype(np.int64) // bs)).sum()) * bs
+        rec["config"]["workload"] = rec["config"]["workload"].replace("block_size 16", f"block_size {bs}")
+        rec["block_size_tradeoff"] = {"block_size": bs, "slot_utilisation": round(int(d.context_lens.sum()) / used_slots, 5),
+                                      "table_bytes": table, "tile_bytes": bs * D * elt}
     if args.workload == "prefix13b":
         rec["aliasing"] = {"path": "shared-prefix decode" if shared else "plain decode",
                            "logical_kv_bytes": logical_kv, "unique_kv_bytes": kv,

@@ -27,7 +27,8 @@
  *      block_tables      int32 [num_seqs][max_blocks_per_seq]
  *      q, out            [rows][num_heads][head_dim]
  *    A slot is block * block_size + offset.
- *  - Supported: head_dim 64 or 128, block_size 16 or 32, num_kv_heads ==
+ *  - Supported: head_dim 64 or 128, block_size 8, 16, 32 or 64 (the pages
+ *    use 16 or 32 and advise against more than 64), num_kv_heads ==
  *    num_heads, dtype f32/f16/bf16; out_dtype is PA_F32 or equal to dtype.
  *    Accumulation is fp32; a narrower output is rounded to nearest even from
  *    the fp32 result.

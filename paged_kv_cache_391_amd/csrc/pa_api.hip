@@ -13,7 +13,7 @@ using pa::Dt;
 bool dtype_ok(pa_dtype d) { return d == PA_F32 || d == PA_F16 || d == PA_BF16; }
 int elt_bytes(pa_dtype d) { return d == PA_F32 ? 4 : 2; }
 bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
-bool block_size_ok(int32_t b) { return b == 16 || b == 32; }
+bool block_size_ok(int32_t b) { return b == 8 || b == 16 || b == 32 || b == 64; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 pa_status hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }

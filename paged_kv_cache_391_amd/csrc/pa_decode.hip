@@ -222,7 +222,8 @@ template <Dt DT, int D, int BS, int HG, RowMode MODE>
 __global__ __launch_bounds__(HG * 64, PA_DECODE_MIN_WAVES) void decode_partition_kernel(const DecodeArgs a) {
   using L = Lane<DT, D>;
   constexpr int WPL = L::WPL;
-  constexpr int TPB = BS / 16;  // tiles per block
+  // a 16-token tile lies in one block (BS >= 16) or in two (BS == 8)
+  constexpr int TPB = BS >= 16 ? BS / 16 : 1;  // tiles per block
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
@@ -272,22 +273,36 @@ __global__ __launch_bounds__(HG * 64, PA_DECODE_MIN_WAVES) void decode_partition
 
   for (int base = 0; base < my_tiles; base += 64) {
     const int cnt = min(64, my_tiles - base);
-    // table entry of tile u0 + base + lane
-    int32_t tb = 0;
-    if (lane < cnt) tb = bt_row[(u0 + base + lane) / TPB];
+    // table entries of tile u0 + base + lane (with 8-token blocks, the
+    // second half of the tile is the next entry, read only if the sequence
+    // has that block; otherwise its rows are past the context and masked)
+    int32_t tb = 0, tb2 = 0;
+    if (lane < cnt) {
+      const int u = u0 + base + lane;
+      if constexpr (BS >= 16) {
+        tb = bt_row[u / TPB];
+      } else {
+        tb = bt_row[2 * u];
+        tb2 = 2 * u + 1 < (ctx + 7) / 8 ? bt_row[2 * u + 1] : tb;
+      }
+    }
 
-    // wave-uniform byte offset of tile i's first row (K and V share it)
-    auto tile_off = [&](int i, int& t0) -> int64_t {
+    // wave-uniform byte offsets of tile i's rows 0-7 and 8-15 (K and V share them)
+    struct TileOff { int64_t lo, hi; };
+    auto tile_off = [&](int i, int& t0) -> TileOff {
       const int u = u0 + base + i;
-      const int32_t phys = __builtin_amdgcn_readlane(tb, i);
       t0 = u * 16;
-      return kv_row_offset(phys, h, (u % TPB) * 16, a.H, BS, D) * L::EB;
+      const int64_t lo = kv_row_offset(__builtin_amdgcn_readlane(tb, i), h, (u % TPB) * 16, a.H, BS, D) * L::EB;
+      if constexpr (BS >= 16) return {lo, lo + 8 * L::ROW_BYTES};
+      else return {lo, kv_row_offset(__builtin_amdgcn_readlane(tb2, i), h, 0, a.H, BS, D) * L::EB};
     };
-    auto load_tile = [&](uint32_t (&kw)[4][WPL], uint32_t (&vw)[4][WPL], int64_t off) {
+    auto load_tile = [&](uint32_t (&kw)[4][WPL], uint32_t (&vw)[4][WPL], TileOff off) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) L::template load<true>(kw[j], kc + off + j * 4 * L::ROW_BYTES, lane_off);
+      for (int j = 0; j < 4; ++j)
+        L::template load<true>(kw[j], kc + (j < 2 ? off.lo : off.hi) + (j & 1) * 4 * L::ROW_BYTES, lane_off);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) L::template load<true>(vw[j], vc + off + j * 4 * L::ROW_BYTES, lane_off);
+      for (int j = 0; j < 4; ++j)
+        L::template load<true>(vw[j], vc + (j < 2 ? off.lo : off.hi) + (j & 1) * 4 * L::ROW_BYTES, lane_off);
       // keep the loads issued here, ahead of the other buffer's math
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -396,12 +411,21 @@ static hipError_t launch_k2(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <Dt DT, int D, RowMode MODE>
+static hipError_t dispatch_k2_bs(const DecodeArgs& a, int BS, hipStream_t stream) {
+  switch (BS) {
+    case 8: return launch_k2<DT, D, 8, MODE>(a, stream);
+    case 16: return launch_k2<DT, D, 16, MODE>(a, stream);
+    case 32: return launch_k2<DT, D, 32, MODE>(a, stream);
+    case 64: return launch_k2<DT, D, 64, MODE>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <Dt DT, RowMode MODE>
 static hipError_t dispatch_k2(const DecodeArgs& a, int D, int BS, hipStream_t stream) {
-  if (D == 128 && BS == 16) return launch_k2<DT, 128, 16, MODE>(a, stream);
-  if (D == 128 && BS == 32) return launch_k2<DT, 128, 32, MODE>(a, stream);
-  if (D == 64 && BS == 16) return launch_k2<DT, 64, 16, MODE>(a, stream);
-  if (D == 64 && BS == 32) return launch_k2<DT, 64, 32, MODE>(a, stream);
+  if (D == 128) return dispatch_k2_bs<DT, 128, MODE>(a, BS, stream);
+  if (D == 64) return dispatch_k2_bs<DT, 64, MODE>(a, BS, stream);
   return hipErrorInvalidValue;
 }
 

@@ -351,12 +351,21 @@ static hipError_t launch_k4(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <Dt DT, int D>
+static hipError_t dispatch_k4_bs(const PrefillArgs& a, int BS, hipStream_t stream) {
+  switch (BS) {
+    case 8: return launch_k4<DT, D, 8>(a, stream);
+    case 16: return launch_k4<DT, D, 16>(a, stream);
+    case 32: return launch_k4<DT, D, 32>(a, stream);
+    case 64: return launch_k4<DT, D, 64>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <Dt DT>
 static hipError_t dispatch_k4(const PrefillArgs& a, int D, int BS, hipStream_t stream) {
-  if (D == 128 && BS == 16) return launch_k4<DT, 128, 16>(a, stream);
-  if (D == 128 && BS == 32) return launch_k4<DT, 128, 32>(a, stream);
-  if (D == 64 && BS == 16) return launch_k4<DT, 64, 16>(a, stream);
-  if (D == 64 && BS == 32) return launch_k4<DT, 64, 32>(a, stream);
+  if (D == 128) return dispatch_k4_bs<DT, 128>(a, BS, stream);
+  if (D == 64) return dispatch_k4_bs<DT, 64>(a, BS, stream);
   return hipErrorInvalidValue;
 }
 

@@ -82,8 +82,8 @@ __global__ __launch_bounds__(64) void shared_prefix_mfma_kernel(const DecodeArgs
   const int32_t tb = lane < nblk ? bt_row[lane] : 0;
   const char* kc = reinterpret_cast<const char*>(a.k_cache);
   const char* vc = reinterpret_cast<const char*>(a.v_cache);
-  // byte offset of partition-relative key `key` (wave-uniform; whole 16-key
-  // subtiles never straddle a block)
+  // byte offset of partition-relative key `key` (wave-uniform); a 16-key
+  // subtile lies in one block, or in two when blocks hold 8 tokens
   auto row_off = [&](int key) -> int64_t {
     const int32_t phys = __builtin_amdgcn_readlane(tb, key / BS);
     return kv_row_offset(phys, h, key % BS, a.H, BS, D) * 2;
@@ -102,7 +102,14 @@ __global__ __launch_bounds__(64) void shared_prefix_mfma_kernel(const DecodeArgs
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       const int sub = k_begin + rel + 16 * sb < k_end ? rel + 16 * sb : rel;
-      const char* base = kc + row_off(sub) + n16 * ROWB + g4 * 16;
+      int64_t row;
+      if constexpr (BS >= 16) {
+        row = row_off(sub) + n16 * ROWB;
+      } else {
+        const int64_t r0 = row_off(sub), r1 = row_off(sub + 8);
+        row = (n16 < 8 ? r0 : r1) + (n16 & 7) * ROWB;
+      }
+      const char* base = kc + row + g4 * 16;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) kf[sb][ks] = *reinterpret_cast<const u32x4*>(base + ks * 64);
     }
@@ -110,8 +117,15 @@ __global__ __launch_bounds__(64) void shared_prefix_mfma_kernel(const DecodeArgs
   auto load_v = [&](u32x4 (&vr)[VCH][2], int s) {
     const int rel = 32 * s;
     const int off1 = k_begin + rel + 16 < k_end ? rel + 16 : rel;
-    const int64_t b0 = row_off(rel), b1 = row_off(off1);
-    const int64_t base = (n16 < 8 ? b0 : b1) + (2 * (n16 & 7)) * ROWB;
+    int64_t base;
+    if constexpr (BS >= 16) {
+      const int64_t b0 = row_off(rel), b1 = row_off(off1);
+      base = (n16 < 8 ? b0 : b1) + (2 * (n16 & 7)) * ROWB;
+    } else {  // keys 2*n16 and 2*n16+1 lie in block n16 / 4 of the step
+      const int64_t c0 = row_off(rel), c1 = row_off(rel + 8), c2 = row_off(off1), c3 = row_off(off1 + 8);
+      const int q4 = n16 >> 2;
+      base = (q4 == 0 ? c0 : q4 == 1 ? c1 : q4 == 2 ? c2 : c3) + (2 * (n16 & 3)) * ROWB;
+    }
 #pragma unroll
     for (int j = 0; j < VCH; ++j)
 #pragma unroll
@@ -258,12 +272,21 @@ static hipError_t launch_shared_mfma(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <Dt DT, int D>
+static hipError_t dispatch_shared_mfma_bs(const DecodeArgs& a, int BS, hipStream_t stream) {
+  switch (BS) {
+    case 8: return launch_shared_mfma<DT, D, 8>(a, stream);
+    case 16: return launch_shared_mfma<DT, D, 16>(a, stream);
+    case 32: return launch_shared_mfma<DT, D, 32>(a, stream);
+    case 64: return launch_shared_mfma<DT, D, 64>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <Dt DT>
 static hipError_t dispatch_shared_mfma(const DecodeArgs& a, int D, int BS, hipStream_t stream) {
-  if (D == 128 && BS == 16) return launch_shared_mfma<DT, 128, 16>(a, stream);
-  if (D == 128 && BS == 32) return launch_shared_mfma<DT, 128, 32>(a, stream);
-  if (D == 64 && BS == 16) return launch_shared_mfma<DT, 64, 16>(a, stream);
-  if (D == 64 && BS == 32) return launch_shared_mfma<DT, 64, 32>(a, stream);
+  if (D == 128) return dispatch_shared_mfma_bs<DT, 128>(a, BS, stream);
+  if (D == 64) return dispatch_shared_mfma_bs<DT, 64>(a, BS, stream);
   return hipErrorInvalidValue;
 }
 

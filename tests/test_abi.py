@@ -57,7 +57,8 @@ def test_reshape_and_cache_validation():
     assert _rc(T=-1) == pa.PA_ERR_INVALID_ARG
     assert _rc(H=0) == pa.PA_ERR_INVALID_ARG
     assert _rc(D=96) == pa.PA_ERR_UNSUPPORTED
-    assert _rc(bs=8) == pa.PA_ERR_UNSUPPORTED
+    assert _rc(bs=12) == pa.PA_ERR_UNSUPPORTED
+    assert _rc(bs=128) == pa.PA_ERR_UNSUPPORTED
     assert _rc(dt=7) == pa.PA_ERR_UNSUPPORTED
     assert _rc(nb=2 ** 28) == pa.PA_ERR_INVALID_ARG  # num_blocks * block_size overflows int32 slots
     assert _rc(T=0, k=NULL, v=NULL, slot=NULL) == pa.PA_OK  # empty write is a no-op
@@ -79,7 +80,7 @@ def test_decode_validation(fn):
     assert _dec(fn, Hkv=1) == pa.PA_ERR_UNSUPPORTED
     assert _dec(fn, odt=2) == pa.PA_ERR_UNSUPPORTED  # bf16 out for f16 in
     assert _dec(fn, D=80) == pa.PA_ERR_UNSUPPORTED
-    assert _dec(fn, bs=64) == pa.PA_ERR_UNSUPPORTED
+    assert _dec(fn, bs=128) == pa.PA_ERR_UNSUPPORTED
     assert _dec(fn, maxctx=8 * 16 + 1) == pa.PA_ERR_INVALID_ARG  # beyond max_blocks_per_seq * block_size
     assert _dec(fn, scale=float("nan")) == pa.PA_ERR_INVALID_ARG
     assert _dec(fn, S=-1) == pa.PA_ERR_INVALID_ARG

@@ -52,7 +52,8 @@ def test_reshape_and_cache_bit_exact(cid):
     assert np.array_equal(bits(host(od.v_cache)), bits(vc_ref))
 
 
-@pytest.mark.parametrize("dtype,H,D,bs", [("f16", 40, 128, 16), ("bf16", 32, 128, 32), ("f32", 2, 64, 16)])
+@pytest.mark.parametrize("dtype,H,D,bs", [("f16", 40, 128, 16), ("bf16", 32, 128, 32), ("f32", 2, 64, 16),
+                                          ("f16", 8, 128, 8), ("bf16", 4, 64, 64)])
 def test_copy_blocks_bit_exact(dtype, H, D, bs):
     """Copy-on-write block copies equal the oracle's bit for bit; blocks that
     are not destinations keep their bits; a pair naming a block outside the
@@ -159,13 +160,14 @@ def _ragged_cases():
         for D in (64, 128):
             for bs in (16, 32):
                 cases.append((dtype, D, bs))
+    cases += [("f16", 128, 8), ("bf16", 128, 64), ("f32", 64, 8), ("f16", 64, 64)]
     return cases
 
 
 @pytest.mark.parametrize("dtype,D,bs", _ragged_cases())
 def test_decode_ragged_lengths(dtype, D, bs):
     P = pa.decode_partition_tokens()
-    ctx = [1, 2, 15, 16, 17, 31, 33, 100, P - 1, P, P + 1, 2 * P + 7, 3 * P]
+    ctx = [1, 2, 7, 8, 9, 15, 16, 17, 31, 33, 63, 64, 65, 100, P - 1, P, P + 1, 2 * P + 7, 3 * P]
     wl = decode_workload(f"ragged_{dtype}_{D}_{bs}", 500 + D + bs, dtype, 3, D, bs, ctx,
                          maxb=math.ceil(max(ctx) / bs) + 2, pool_factor=1.3)
     od = _on_device_written(wl)
@@ -326,11 +328,12 @@ def _grouped_batch(dtype, bs, groups, seed):
     return kc, vc, q, bt, ctx, np.array(gs, dtype=np.int32), np.array(pl, dtype=np.int32)
 
 
-@pytest.mark.parametrize("dtype,bs", [("f16", 16), ("bf16", 32), ("f16", 32), ("f32", 16)])
+@pytest.mark.parametrize("dtype,bs", [("f16", 16), ("bf16", 32), ("f16", 32), ("f32", 16), ("f16", 8),
+                                      ("bf16", 64)])
 def test_shared_prefix_decode_ragged_groups(dtype, bs):
     groups = [(1, 0, [37]), (3, bs, [0, 5, 700]), (8, 512, [0] * 4 + [1, 16, 300, 513]),
-              (11, 1056 if bs == 16 else 1024, [int(x) for x in np.arange(11) * 37]), (2, 512, [0, 0]),
-              (5, 0, [1, 2, 3, 600, 1200])]
+              (11, 1056 if bs in (8, 16) else 1024, [int(x) for x in np.arange(11) * 37]), (2, 512, [0, 0]),
+              (5, 0, [1, 2, 3, 600, 1200]), (4, 520 if bs == 8 else 512, [9, 0, 33, 64])]
     kc, vc, q, bt, ctx, gs, pl = _grouped_batch(dtype, bs, groups, 31 + bs)
     H, D = q.shape[1], q.shape[2]
     scale = 1 / math.sqrt(D)
@@ -351,7 +354,7 @@ def test_shared_prefix_decode_ragged_groups(dtype, bs):
 # ----------------------------------------------------------------- prefill
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
-@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("bs", [8, 16, 32, 64])
 def test_prefill_parity_small_chunks(dtype, bs):
     prior = [0, 5, 33, 100, 0, 300]
     chunk = [1, 17, 64, 130, 200, 77]

@@ -303,11 +303,14 @@ def config1(seed=None) -> Workload:
     return decode_workload("tiny", seed, "f32", 2, 64, 16, [1, 17, 33, 100], maxb=7, pool_blocks=64)
 
 
-def config2(seed=None, num_seqs=64) -> Workload:
+def config2(seed=None, num_seqs=64, block_size=16) -> Workload:
+    """LLaMA-7B layer decode; ``block_size`` other than 16 keeps the same
+    lengths and values (for the block-size trade-off)."""
     seed = BASE_SEED + 2 if seed is None else seed
     st = _streams(seed)
     ctx = st["lengths"].integers(128, 2048, size=num_seqs, endpoint=True)
-    return decode_workload("llama7b", seed, "f16", 32, 128, 16, ctx, maxb=128, streams=st)
+    return decode_workload("llama7b", seed, "f16", 32, 128, block_size, ctx, maxb=-(-2048 // block_size),
+                           streams=st)
 
 
 def lognormal_lengths(rng, n, mean=600.0, sigma=1.0, lo=1, hi=4096):
