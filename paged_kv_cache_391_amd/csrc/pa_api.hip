@@ -220,7 +220,9 @@ pa_status pa_paged_attention_decode(void* out, pa_dtype out_dtype, const void* q
 size_t pa_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                         int32_t max_context_len) {
   if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
-  const int64_t slots = max_parts_for(max_context_len) + 1;  // shared + own partitions of one row
+  // shared + own partitions of one row: ceil(p / shared) + ceil((ctx - p) / own) for a prefix of p
+  // tokens, at most ceil(ctx / own) + 1 as shared partitions are no shorter than own ones
+  const int64_t slots = max_parts_for(max_context_len) + 1;
   return (size_t)num_seqs * num_heads * slots * (head_dim + 2) * sizeof(float);
 }
 
@@ -263,6 +265,7 @@ pa_status pa_paged_attention_decode_shared_prefix(
   a.max_blocks = max_blocks_per_seq;
   a.ws_parts = (int)parts + 1;
   a.part_tiles = pa::kPartitionTokens / 16;
+  a.shared_part_tiles = pa::shared_partition_tokens(block_size) / 16;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.out_f32 = out_dtype == PA_F32 ? 1 : 0;
   a.group_starts = group_starts;
@@ -272,11 +275,12 @@ pa_status pa_paged_attention_decode_shared_prefix(
   hipError_t e = hipSuccess;
   if (dtype != PA_F32 && max_prefix_len > 0) {
     a.member_chunks = (int)ceil_div(max_group_size, pa::kSharedMembersPerWave);
-    a.max_parts = (int)max_parts_for(max_prefix_len);
-    if ((int64_t)num_groups * a.member_chunks * num_heads * a.max_parts > INT32_MAX) return PA_ERR_INVALID_ARG;
-    e = pa::launch_shared_prefix_mfma(a, dt, head_dim, block_size, stream);
+    const int64_t shared_parts = ceil_div(max_prefix_len, pa::shared_partition_tokens(block_size));
+    if ((int64_t)num_groups * a.member_chunks * num_heads * shared_parts + (int64_t)num_seqs * num_heads * parts >
+        INT32_MAX)
+      return PA_ERR_INVALID_ARG;
     a.max_parts = (int)parts;
-    if (e == hipSuccess) e = pa::launch_decode_partitions(a, dt, head_dim, block_size, pa::RowMode::SharedTail, stream);
+    e = pa::launch_shared_prefix_step(a, dt, head_dim, block_size, (int)shared_parts, (int)parts, stream);
     if (e == hipSuccess) e = pa::launch_decode_reduce(a, dt, head_dim, true, stream);
   } else {
     // nothing shared to exploit (or f32): the ordinary split-K decode

@@ -1,0 +1,345 @@
+// Device-side building blocks of paged decode, shared by the decode kernels
+// (partition, reduction) and the shared-prefix step kernel: the lane
+// mapping of a token row onto a 16-lane DPP row, the per-row online
+// softmax, row layouts of each row mode and the partition kernel's body.
+// Included by pa_decode.hip and pa_shared.hip only.
+#pragma once
+
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+
+template <Dt DT, int D> struct Lane {
+  static constexpr int EB = ElemT<DT>::bytes;
+  static constexpr int BYTES = D * EB / 16;         // bytes of a row owned by one lane
+  static constexpr int WPL = BYTES / 4;             // 32-bit words per lane per row
+  static constexpr int VB = BYTES >= 16 ? 16 : 8;   // bytes per load
+  static constexpr int NV = BYTES / VB;             // loads per lane per row
+  static constexpr int VW = VB / 4;                 // words per load
+  static constexpr int EPW = 4 / EB;                // elements per word
+  static constexpr int VE = VB / EB;                // elements per load
+  static constexpr int EPL = D / 16;                // elements per lane
+  static constexpr int ROW_WORDS = D * EB / 4;
+
+  static constexpr int ROW_BYTES = D * EB;
+
+  // element index (within the head's D) of the lane's k-th element
+  __device__ static __forceinline__ int elem(int c, int k) { return (k / VE) * 16 * VE + c * VE + (k % VE); }
+
+  // The lane's words of one row. `base` is wave-uniform (scalar registers)
+  // and `lane_off` a loop-invariant per-lane byte offset, so the loads use
+  // the scalar-base + vector-offset form and every tile's address is formed
+  // with scalar arithmetic only. Load j of the lane covers 16*VB contiguous
+  // bytes together with the other 15 lanes of its row.
+  template <bool NT = false>
+  __device__ static __forceinline__ void load(uint32_t (&w)[WPL], const char* base, uint32_t lane_off) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      if constexpr (VB == 16) {
+        const u32x4 x = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + lane_off + j * 16 * VB))
+                           : *reinterpret_cast<const u32x4*>(base + lane_off + j * 16 * VB);
+        w[j * 4 + 0] = x[0]; w[j * 4 + 1] = x[1]; w[j * 4 + 2] = x[2]; w[j * 4 + 3] = x[3];
+      } else {
+        const u32x2 x = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base + lane_off + j * 16 * VB))
+                           : *reinterpret_cast<const u32x2*>(base + lane_off + j * 16 * VB);
+        w[j * 2 + 0] = x[0]; w[j * 2 + 1] = x[1];
+      }
+    }
+  }
+
+  __device__ static __forceinline__ float dot(const uint32_t (&q)[WPL], const uint32_t (&k)[WPL]) {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < WPL; ++i) {
+      if constexpr (DT == Dt::F16)
+        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, q[i]), __builtin_bit_cast(half2_t, k[i]), acc,
+                                     false);
+      else if constexpr (DT == Dt::BF16)
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, q[i]), __builtin_bit_cast(bf162_t, k[i]),
+                                              acc, false);
+      else
+        acc = fmaf(__uint_as_float(q[i]), __uint_as_float(k[i]), acc);
+    }
+    return acc;
+  }
+
+  // acc[k] += p * v[k]
+  __device__ static __forceinline__ void axpy(float (&acc)[EPL], float p, const uint32_t (&v)[WPL]) {
+#pragma unroll
+    for (int i = 0; i < WPL; ++i) {
+      if constexpr (EPW == 2) {
+        acc[2 * i] = fmaf(p, widen_lo<DT>(v[i]), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(p, widen_hi<DT>(v[i]), acc[2 * i + 1]);
+      } else {
+        acc[i] = fmaf(p, __uint_as_float(v[i]), acc[i]);
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Online-softmax state of one 16-lane row of a wave.
+template <int EPL> struct Soft {
+  float m;
+  float l;
+  float acc[EPL];
+};
+
+// Consume one 16-token tile: token 4*j + g of the tile is in K[j]/V[j].
+template <Dt DT, int D>
+__device__ __forceinline__ void consume_tile(Soft<D / 16>& st, const uint32_t (&qw)[Lane<DT, D>::WPL],
+                                             const uint32_t (&kw)[4][Lane<DT, D>::WPL],
+                                             const uint32_t (&vw)[4][Lane<DT, D>::WPL], int t0, int ctx, int g,
+                                             float scale_log2) {
+  using L = Lane<DT, D>;
+  float s[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) s[j] = row16_sum(L::dot(qw, kw[j])) * scale_log2;
+  const bool partial = t0 + 16 > ctx;
+  bool valid[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    valid[j] = !partial || (t0 + 4 * j + g < ctx);
+    s[j] = valid[j] ? s[j] : -INFINITY;
+  }
+  const float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  const float m_new = fmaxf(st.m, mt);
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = fast_exp2(st.m - m_use);
+  float p[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) p[j] = fast_exp2(s[j] - m_use);
+  st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+#pragma unroll
+  for (int k = 0; k < L::EPL; ++k) st.acc[k] *= alpha;
+  // Slots past the context may hold anything (even NaN): select zeros for
+  // them instead of multiplying (0 * NaN would poison the sum). Selects on
+  // every tile, not a branch for the last one, keep the instruction stream
+  // straight so the compiler's load-wait counts stay exact.
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t vz[L::WPL];
+#pragma unroll
+    for (int i = 0; i < L::WPL; ++i) vz[i] = valid[j] ? vw[j][i] : 0u;
+    L::axpy(st.acc, p[j], vz);
+  }
+  st.m = m_new;
+}
+
+template <Dt DT>
+__device__ __forceinline__ void store_out(void* out, int64_t idx, float x, int out_f32) {
+  if (out_f32 || DT == Dt::F32) {
+    reinterpret_cast<float*>(out)[idx] = x;
+  } else {
+    const uint32_t b = DT == Dt::F16 ? f32_to_f16_bits(x) : f32_to_bf16_bits(x);
+    reinterpret_cast<uint16_t*>(out)[idx] = (uint16_t)b;
+  }
+}
+
+// Row r of the prefill-row mode is query j of chunk s: its causal context is
+// ctx[s] - L_s + j + 1 tokens of sequence s.
+__device__ __forceinline__ void prefill_row(const int32_t* qsl, const int32_t* ctx_lens, int S, int r, int& seq,
+                                            int& ctx) {
+  int lo = 0, hi = S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (qsl[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  seq = lo;
+  const int L = qsl[lo + 1] - qsl[lo];
+  ctx = ctx_lens[lo] - L + (r - qsl[lo]) + 1;
+}
+
+// Group g of a prefix-sharing batch is rows group_starts[g] .. group_starts[g+1]-1.
+__device__ __forceinline__ int group_of_row(const int32_t* group_starts, int num_groups, int r) {
+  int lo = 0, hi = num_groups - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (group_starts[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Partition layout of one row: own partitions cover tokens [tok0, ctx) in
+// part_tiles-tile steps and sit in workspace slots poff, poff+1, ...; a row
+// of a prefix-sharing group has ceil(prefix / shared partition) shared
+// partitions (written by the shared-prefix kernel) in slots 0 .. poff-1.
+struct RowParts {
+  int tok0, own, poff;
+  __device__ __forceinline__ int total() const { return poff + own; }
+};
+template <RowMode MODE>
+__device__ __forceinline__ RowParts row_parts(const DecodeArgs& a, int row, int ctx) {
+  RowParts rp{0, 0, 0};
+  if constexpr (MODE == RowMode::SharedTail) {
+    // the prefix is whole tiles inside the row (clamped so that a prefix
+    // longer than the row can never send a read past the row's blocks)
+    const int p = min(a.prefix_lens[group_of_row(a.group_starts, a.num_groups, row)], ctx) & ~15;
+    const int pt = a.shared_part_tiles * 16;
+    rp.tok0 = p;
+    rp.poff = (p + pt - 1) / pt;
+  }
+  const int own_tiles = ((ctx + 15) >> 4) - (rp.tok0 >> 4);
+  rp.own = (own_tiles + a.part_tiles - 1) / a.part_tiles;
+  return rp;
+}
+
+}  // namespace
+
+// Body of the partition kernel for workgroup `bid` (wave `wave` of HG takes
+// head hg*HG + wave); shared by the partition kernel and the shared-prefix
+// step kernel.
+template <Dt DT, int D, int BS, int HG, RowMode MODE>
+__device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int bid, int wave) {
+  using L = Lane<DT, D>;
+  constexpr int WPL = L::WPL;
+  // a 16-token tile lies in one block (BS >= 16) or in two (BS == 8)
+  constexpr int TPB = BS >= 16 ? BS / 16 : 1;  // tiles per block
+
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const int c = lane & 15;
+
+  // grid: partition-major, then row, then head group; wave w takes head hg*HG + w
+  const int n_hg = (a.H + HG - 1) / HG;
+  const int hg = bid % n_hg;
+  bid /= n_hg;
+  const int row = bid % a.num_rows;
+  const int part = bid / a.num_rows;
+  const int h = hg * HG + wave;
+  if (h >= a.H) return;
+
+  int seq, ctx;
+  if constexpr (MODE == RowMode::PrefillRows) {
+    prefill_row(a.query_start_loc, a.context_lens, a.num_seqs, row, seq, ctx);
+  } else {
+    seq = row;
+    ctx = a.context_lens[row];
+  }
+  const int n_tiles = (ctx + 15) >> 4;
+  const RowParts rp = row_parts<MODE>(a, row, ctx);
+  // partition 0 of an empty row still runs (it writes zeros), except for the
+  // tail of a shared prefix that covers the whole row
+  if (part >= (rp.own > 0 ? rp.own : (rp.poff > 0 ? 0 : 1))) return;
+
+  const int u0 = (rp.tok0 >> 4) + part * a.part_tiles;
+  const int my_tiles = max(0, min(n_tiles, u0 + a.part_tiles) - u0);
+
+  uint32_t qw[WPL];
+  L::load(qw, reinterpret_cast<const char*>(a.q) + ((int64_t)row * a.H + h) * L::ROW_BYTES, (uint32_t)(c * L::VB));
+
+  Soft<L::EPL> st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int k = 0; k < L::EPL; ++k) st.acc[k] = 0.f;
+
+  const int32_t* bt_row = a.block_tables + (int64_t)seq * a.max_blocks;
+  const char* kc = reinterpret_cast<const char*>(a.k_cache);
+  const char* vc = reinterpret_cast<const char*>(a.v_cache);
+  // row g of a 4-row group, lane chunk c
+  const uint32_t lane_off = (uint32_t)(g * L::ROW_BYTES + c * L::VB);
+
+  for (int base = 0; base < my_tiles; base += 64) {
+    const int cnt = min(64, my_tiles - base);
+    // table entries of tile u0 + base + lane (with 8-token blocks, the
+    // second half of the tile is the next entry, read only if the sequence
+    // has that block; otherwise its rows are past the context and masked)
+    int32_t tb = 0, tb2 = 0;
+    if (lane < cnt) {
+      const int u = u0 + base + lane;
+      if constexpr (BS >= 16) {
+        tb = bt_row[u / TPB];
+      } else {
+        tb = bt_row[2 * u];
+        tb2 = 2 * u + 1 < (ctx + 7) / 8 ? bt_row[2 * u + 1] : tb;
+      }
+    }
+
+    // wave-uniform byte offsets of tile i's rows 0-7 and 8-15 (K and V share them)
+    struct TileOff { int64_t lo, hi; };
+    auto tile_off = [&](int i, int& t0) -> TileOff {
+      const int u = u0 + base + i;
+      t0 = u * 16;
+      const int64_t lo = kv_row_offset(__builtin_amdgcn_readlane(tb, i), h, (u % TPB) * 16, a.H, BS, D) * L::EB;
+      if constexpr (BS >= 16) return {lo, lo + 8 * L::ROW_BYTES};
+      else return {lo, kv_row_offset(__builtin_amdgcn_readlane(tb2, i), h, 0, a.H, BS, D) * L::EB};
+    };
+    auto load_tile = [&](uint32_t (&kw)[4][WPL], uint32_t (&vw)[4][WPL], TileOff off) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        L::template load<true>(kw[j], kc + (j < 2 ? off.lo : off.hi) + (j & 1) * 4 * L::ROW_BYTES, lane_off);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        L::template load<true>(vw[j], vc + (j < 2 ? off.lo : off.hi) + (j & 1) * 4 * L::ROW_BYTES, lane_off);
+      // keep the loads issued here, ahead of the other buffer's math
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Two register buffers, next tile always in flight. The steady-state
+    // loop body has no branch, so the compiler's wait counts stay exact and
+    // never drain the load queue; the last one or two tiles are finished
+    // after it, so every tile is fetched exactly once.
+    uint32_t ka[4][WPL], va[4][WPL], kb[4][WPL], vb[4][WPL];
+    int ta, tb0;
+    load_tile(ka, va, tile_off(0, ta));
+    int i = 0;
+    for (; i + 2 < cnt; i += 2) {
+      load_tile(kb, vb, tile_off(i + 1, tb0));
+      consume_tile<DT, D>(st, qw, ka, va, ta, ctx, g, a.scale_log2);
+      load_tile(ka, va, tile_off(i + 2, ta));
+      consume_tile<DT, D>(st, qw, kb, vb, tb0, ctx, g, a.scale_log2);
+    }
+    if (i + 1 < cnt) {
+      load_tile(kb, vb, tile_off(i + 1, tb0));
+      consume_tile<DT, D>(st, qw, ka, va, ta, ctx, g, a.scale_log2);
+      consume_tile<DT, D>(st, qw, kb, vb, tb0, ctx, g, a.scale_log2);
+    } else {
+      consume_tile<DT, D>(st, qw, ka, va, ta, ctx, g, a.scale_log2);
+    }
+  }
+
+  // merge the four 16-lane rows of the wave (same lane column c)
+  float m_all = fmaxf(st.m, shfl_xor_f(st.m, 16));
+  m_all = fmaxf(m_all, shfl_xor_f(m_all, 32));
+  {
+    const float f = fast_exp2(st.m - (m_all == -INFINITY ? 0.f : m_all));
+    float lw = st.l * f;
+    lw += shfl_xor_f(lw, 16);
+    lw += shfl_xor_f(lw, 32);
+    st.l = lw;
+#pragma unroll
+    for (int k = 0; k < L::EPL; ++k) {
+      float x = st.acc[k] * f;
+      x += shfl_xor_f(x, 16);
+      x += shfl_xor_f(x, 32);
+      st.acc[k] = x;
+    }
+    st.m = m_all;
+  }
+  if (g != 0) return;
+
+  const int64_t orow = ((int64_t)row * a.H + h) * D;
+  if (rp.total() <= 1) {
+#pragma unroll
+    for (int k = 0; k < L::EPL; ++k) {
+      const float o = st.l > 0.f ? st.acc[k] / st.l : 0.f;
+      store_out<DT>(a.out, orow + L::elem(c, k), o, a.out_f32);
+    }
+  } else {
+    const int64_t prow = ((int64_t)row * a.H + h) * a.ws_parts + rp.poff + part;
+    float* acc_out = a.ws + prow * D;
+#pragma unroll
+    for (int k = 0; k < L::EPL; ++k) acc_out[L::elem(c, k)] = st.acc[k];
+    if (c == 0) {
+      float* ml = a.ws + (int64_t)a.num_rows * a.H * a.ws_parts * D + prow * 2;
+      ml[0] = st.m;
+      ml[1] = st.l;
+    }
+  }
+}
+
+}  // namespace pa

@@ -19,12 +19,29 @@
 #ifndef PA_PARTITION_TOKENS
 #define PA_PARTITION_TOKENS 512
 #endif
+#ifndef PA_SHARED_PARTITION_TOKENS
+#define PA_SHARED_PARTITION_TOKENS 1024
+#endif
 
 namespace pa {
 
 constexpr int kDecodeHeadsPerGroup = PA_DECODE_HEADS;
 constexpr int kPartitionTokens = PA_PARTITION_TOKENS;
 static_assert(kPartitionTokens % 32 == 0, "partitions must hold whole 16- and 32-token blocks");
+// Shared prefixes are split coarser than private tokens: a shared wave serves
+// up to 16 members, and fewer, longer shared waves measured faster (less
+// set-up and fewer partials per member). A shared partition is at most 64
+// blocks (the table entries one wave holds in its lanes), so its length is
+// min(kSharedPartitionTokens, 64 * block_size) -- never below
+// kPartitionTokens for the supported block sizes, which keeps a row's
+// shared + own partitions within ceil(ctx / kPartitionTokens) + 1 slots.
+constexpr int kSharedPartitionTokens = PA_SHARED_PARTITION_TOKENS;
+static_assert(kSharedPartitionTokens % 32 == 0 && kSharedPartitionTokens >= kPartitionTokens &&
+                  64 * 8 >= kPartitionTokens,
+              "shared partitions must hold whole 32-token steps and no fewer tokens than a private one");
+inline int shared_partition_tokens(int block_size) {
+  return kSharedPartitionTokens < 64 * block_size ? kSharedPartitionTokens : 64 * block_size;
+}
 
 // Which rows a partition-kernel launch walks.
 enum class RowMode : int {
@@ -49,6 +66,7 @@ struct DecodeArgs {
   int max_parts;                    // partitions per row in the grid
   int ws_parts;                     // partition slots per (row, head) in the workspace
   int part_tiles;                   // 16-token tiles per partition
+  int shared_part_tiles;            // 16-token tiles per shared-prefix partition
   const int32_t* group_starts;      // SharedTail / shared-prefix kernel: [num_groups+1] row ranges
   const int32_t* prefix_lens;       // [num_groups] shared tokens (whole 16-token tiles)
   int num_groups;
@@ -71,9 +89,12 @@ hipError_t launch_gather_kv(void* k_out, void* v_out, const void* k_cache, const
 hipError_t launch_decode_partitions(const DecodeArgs& a, Dt dt, int D, int BS, RowMode mode, hipStream_t stream);
 // reduction kernel (K3); shared = rows carry a shared-prefix partition offset
 hipError_t launch_decode_reduce(const DecodeArgs& a, Dt dt, int D, bool shared, hipStream_t stream);
-// shared-prefix partitions on the matrix cores: each shared K/V tile is read
-// once per group, one wave per 16 members (f16/bf16)
-hipError_t launch_shared_prefix_mfma(const DecodeArgs& a, Dt dt, int D, int BS, hipStream_t stream);
+// shared-prefix decode before the reduction, in one launch: the shared
+// prefixes on the matrix cores (each shared K/V tile read once per group, one
+// wave per 16 members; shared_parts partitions) next to the members' private
+// tails (SharedTail rows; tail_parts partitions), f16/bf16
+hipError_t launch_shared_prefix_step(const DecodeArgs& a, Dt dt, int D, int BS, int shared_parts, int tail_parts,
+                                     hipStream_t stream);
 constexpr int kSharedMembersPerWave = 16;
 
 // MFMA causal prefill (K4), fp16/bf16 only

@@ -22,7 +22,7 @@
 // masks. Each member gets (m, l, acc[D]) for this partition in the split-K
 // workspace (or its final output when the partition is all it has); its
 // private tail and the merge run in the partition and reduction kernels.
-#include "pa_internal.h"
+#include "pa_decode_device.h"
 
 namespace pa {
 
@@ -31,7 +31,7 @@ constexpr float kRescaleLog2 = 8.f;  // p = 2^(s - m) stays below 2^8 between re
 }
 
 template <Dt DT, int D, int BS>
-__global__ __launch_bounds__(64) void shared_prefix_mfma_kernel(const DecodeArgs a) {
+__device__ __forceinline__ void shared_prefix_body(const DecodeArgs& a, int bid) {
   constexpr int KS = D / 32;      // MFMA k-steps over head_dim for S^T = K Q^T
   constexpr int NDT = D / 16;     // 16-row blocks of O^T
   constexpr int ROWB = D * 2;     // bytes of one K/V row (16-bit elements)
@@ -46,7 +46,6 @@ __global__ __launch_bounds__(64) void shared_prefix_mfma_kernel(const DecodeArgs
   const int g4 = lane >> 4;
 
   // grid: partition-major, then group, member chunk, head
-  int bid = blockIdx.x;
   const int h = bid % a.H;
   bid /= a.H;
   const int mc = bid % a.member_chunks;
@@ -58,7 +57,7 @@ __global__ __launch_bounds__(64) void shared_prefix_mfma_kernel(const DecodeArgs
   const int m0 = r_begin + 16 * mc;
   const int nm = min(16, a.group_starts[grp + 1] - m0);
   if (nm <= 0) return;
-  const int pt = a.part_tiles * 16;
+  const int pt = a.shared_part_tiles * 16;
   const int prefix = min(a.prefix_lens[grp], a.context_lens[r_begin]) & ~15;  // whole tiles of the first member
   const int ns = (prefix + pt - 1) / pt;
   if (part >= ns) return;
@@ -264,35 +263,51 @@ __global__ __launch_bounds__(64) void shared_prefix_mfma_kernel(const DecodeArgs
   }
 }
 
+// One launch for the whole shared-prefix decode (before the reduction):
+// workgroups [0, n_shared) run the shared prefixes on the matrix cores,
+// the rest run the members' private tails as partition-kernel waves (one
+// head per workgroup), so the two kinds of work overlap on the chip instead
+// of running one after the other.
 template <Dt DT, int D, int BS>
-static hipError_t launch_shared_mfma(const DecodeArgs& a, hipStream_t stream) {
-  const int64_t grid = (int64_t)a.num_groups * a.member_chunks * a.H * a.max_parts;
+__global__ __launch_bounds__(64) void shared_prefix_step_kernel(const DecodeArgs a, int n_shared) {
+  if ((int)blockIdx.x < n_shared)
+    shared_prefix_body<DT, D, BS>(a, blockIdx.x);
+  else
+    decode_partition_body<DT, D, BS, 1, RowMode::SharedTail>(a, blockIdx.x - n_shared, 0);
+}
+
+template <Dt DT, int D, int BS>
+static hipError_t launch_step(const DecodeArgs& a, int shared_parts, int tail_parts, hipStream_t stream) {
+  const int64_t n_shared = (int64_t)a.num_groups * a.member_chunks * a.H * shared_parts;
+  const int64_t grid = n_shared + (int64_t)a.num_rows * a.H * tail_parts;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((shared_prefix_mfma_kernel<DT, D, BS>), dim3((unsigned)grid), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL((shared_prefix_step_kernel<DT, D, BS>), dim3((unsigned)grid), dim3(64), 0, stream, a,
+                     (int)n_shared);
   return hipGetLastError();
 }
 
 template <Dt DT, int D>
-static hipError_t dispatch_shared_mfma_bs(const DecodeArgs& a, int BS, hipStream_t stream) {
+static hipError_t dispatch_step_bs(const DecodeArgs& a, int BS, int sp, int tp, hipStream_t stream) {
   switch (BS) {
-    case 8: return launch_shared_mfma<DT, D, 8>(a, stream);
-    case 16: return launch_shared_mfma<DT, D, 16>(a, stream);
-    case 32: return launch_shared_mfma<DT, D, 32>(a, stream);
-    case 64: return launch_shared_mfma<DT, D, 64>(a, stream);
+    case 8: return launch_step<DT, D, 8>(a, sp, tp, stream);
+    case 16: return launch_step<DT, D, 16>(a, sp, tp, stream);
+    case 32: return launch_step<DT, D, 32>(a, sp, tp, stream);
+    case 64: return launch_step<DT, D, 64>(a, sp, tp, stream);
   }
   return hipErrorInvalidValue;
 }
 
 template <Dt DT>
-static hipError_t dispatch_shared_mfma(const DecodeArgs& a, int D, int BS, hipStream_t stream) {
-  if (D == 128) return dispatch_shared_mfma_bs<DT, 128>(a, BS, stream);
-  if (D == 64) return dispatch_shared_mfma_bs<DT, 64>(a, BS, stream);
+static hipError_t dispatch_step(const DecodeArgs& a, int D, int BS, int sp, int tp, hipStream_t stream) {
+  if (D == 128) return dispatch_step_bs<DT, 128>(a, BS, sp, tp, stream);
+  if (D == 64) return dispatch_step_bs<DT, 64>(a, BS, sp, tp, stream);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_shared_prefix_mfma(const DecodeArgs& a, Dt dt, int D, int BS, hipStream_t stream) {
-  if (dt == Dt::F16) return dispatch_shared_mfma<Dt::F16>(a, D, BS, stream);
-  if (dt == Dt::BF16) return dispatch_shared_mfma<Dt::BF16>(a, D, BS, stream);
+hipError_t launch_shared_prefix_step(const DecodeArgs& a, Dt dt, int D, int BS, int shared_parts, int tail_parts,
+                                     hipStream_t stream) {
+  if (dt == Dt::F16) return dispatch_step<Dt::F16>(a, D, BS, shared_parts, tail_parts, stream);
+  if (dt == Dt::BF16) return dispatch_step<Dt::BF16>(a, D, BS, shared_parts, tail_parts, stream);
   return hipErrorInvalidValue;
 }
 

@@ -333,7 +333,8 @@ def _grouped_batch(dtype, bs, groups, seed):
 def test_shared_prefix_decode_ragged_groups(dtype, bs):
     groups = [(1, 0, [37]), (3, bs, [0, 5, 700]), (8, 512, [0] * 4 + [1, 16, 300, 513]),
               (11, 1056 if bs in (8, 16) else 1024, [int(x) for x in np.arange(11) * 37]), (2, 512, [0, 0]),
-              (5, 0, [1, 2, 3, 600, 1200]), (4, 520 if bs == 8 else 512, [9, 0, 33, 64])]
+              (5, 0, [1, 2, 3, 600, 1200]), (4, 520 if bs == 8 else 512, [9, 0, 33, 64]),
+              (3, 2112 if bs >= 32 else 1040, [0, 7, 530])]  # several shared partitions at every block size
     kc, vc, q, bt, ctx, gs, pl = _grouped_batch(dtype, bs, groups, 31 + bs)
     H, D = q.shape[1], q.shape[2]
     scale = 1 / math.sqrt(D)
