@@ -28,9 +28,11 @@ side stream next to the decode (the in-order graph is timed too).
 
 Prints ONE JSON line: value = algorithmic bytes of the step / step time
 (GB/s, 1e9 B/s); roofline = the decode partition kernel's algorithmic bytes
-over its average launch time (HIP events on the launch stream) against the
-8 TB/s HBM peak; cpu_baseline = the fp64 oracle on the host cores over the
-same work.
+over its average launch time against the 8 TB/s HBM peak, timed with HIP
+events on the launch stream in a cold-cache pass (a 1 GiB read before every
+step evicts L2 and the memory-side cache; the warm back-to-back average is
+reported next to it); cpu_baseline = the fp64 oracle on the host cores over
+the same work, and on one thread over a sample of it.
 """
 import argparse
 import hashlib
@@ -47,7 +49,7 @@ METRIC = "paged decode attention achieved HBM GB/s (% of peak) at LLaMA-7B layer
 METRIC_OTHER = "paged attention step achieved HBM GB/s (% of peak)"
 HBM_PEAK_GBPS = 8000.0
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # dense fp16/bf16 matrix-core peak of MI355X
-KERNEL_SOURCES = ["pa_decode.hip", "pa_device.h", "pa_internal.h"]
+KERNEL_SOURCES = ["pa_decode.hip", "pa_decode_device.h", "pa_device.h", "pa_internal.h"]
 CPU_SECONDS = 10.0  # the oracle repeats its pass until about this much CPU time has elapsed
 
 WORKLOADS = {
@@ -168,34 +170,76 @@ def prefill_work(p, H, D, elt):
     return flops, byts
 
 
-def cpu_baseline(wl, threads, alg_bytes):
-    """The fp64 oracle, as it stands, over the same decode (and prefill)
-    work, repeated until about CPU_SECONDS have elapsed; its rate uses the
-    same algorithmic byte count as the GPU step's value."""
+def _host_cpu():
+    """Model name of the host CPU (first entry of /proc/cpuinfo) and the
+    cores this process may run on."""
+    name = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    name = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return name, avail
+
+
+def _oracle_rate(wl, kc, vc, rows, threads, seconds, byts):
+    """GB/s of the oracle's decode (and, with every row, its prefill) over
+    the first `rows` decode sequences, whose algorithmic bytes are `byts`,
+    repeated until `seconds` have elapsed."""
+    import numpy as np
     import oracle
-    kc, vc = oracle.reshape_and_cache(wl.new.k, wl.new.v, wl.k_cache, wl.v_cache, wl.new.slot_mapping,
-                                      wl.block_size, wl.dtype)
     d, p = wl.decode, wl.prefill
+    whole = rows >= d.num_seqs
+    q, bt, ctx = d.q[:rows], d.block_tables[:rows], d.context_lens[:rows]
 
     def one_pass():
-        if p is not None:
+        if whole and p is not None:
             oracle.prefill(p.q, kc, vc, p.block_tables, p.context_lens, p.query_start_loc, wl.scale, wl.dtype,
                            threads=threads)
-        oracle.decode(d.q, kc, vc, d.block_tables, d.context_lens, wl.scale, wl.dtype, threads=threads)
+        oracle.decode(q, kc, vc, bt, ctx, wl.scale, wl.dtype, threads=threads)
 
     reps, t0 = 0, time.perf_counter()
     while True:
         one_pass()
         reps += 1
         el = time.perf_counter() - t0
-        if el >= CPU_SECONDS or reps >= 1000:
+        if el >= seconds or reps >= 1000:
             break
     per = el / reps
-    byts = alg_bytes
-    what = "prefill of the 4 chunks + decode" if p is not None else "the whole decode"
-    return {"value": round(byts / per / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    return byts / per / 1e9, reps, el, per, int(np.asarray(ctx, dtype=np.int64).sum())
+
+
+def cpu_baseline(wl, threads, alg_bytes, sample_bytes):
+    """The fp64 oracle, as it stands, on the host: all usable cores (up to
+    16) over the step's whole decode (and prefill), then one thread over a
+    bounded sample (the first eighth of the decode sequences); each repeated
+    until about CPU_SECONDS have elapsed. Rates use the same algorithmic-byte
+    definition as the GPU step's value: `alg_bytes` for the whole work,
+    `sample_bytes(rows)` for the decode of the first `rows` sequences."""
+    import oracle
+    kc, vc = oracle.reshape_and_cache(wl.new.k, wl.new.v, wl.k_cache, wl.v_cache, wl.new.slot_mapping,
+                                      wl.block_size, wl.dtype)
+    S = wl.decode.num_seqs
+    rate, reps, el, per, _ = _oracle_rate(wl, kc, vc, S, threads, CPU_SECONDS, alg_bytes)
+    rows1 = max(1, S // 8)
+    rate1, reps1, el1, per1, tok1 = _oracle_rate(wl, kc, vc, rows1, 1, CPU_SECONDS, sample_bytes(rows1))
+    model, avail = _host_cpu()
+    what = "prefill of the 4 chunks + decode" if wl.prefill is not None else "the whole decode"
+    return {"value": round(rate, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{what} of this workload, {reps} pass(es) in {el:.1f} s ({per:.3f} s each); fp64, gather + "
-                      "softmax attention per (row, head), OpenMP over pairs; same algorithmic-byte count as value"}
+                      "softmax attention per (row, head), OpenMP over pairs; same algorithmic-byte definition as "
+                      "value",
+            "one_thread": {"value": round(rate1, 3), "unit": "GB/s", "cores": 1,
+                           "sample": f"decode of the first {rows1} of {S} sequences ({tok1} context tokens), "
+                                     f"{reps1} pass(es) in {el1:.1f} s ({per1:.3f} s each)"},
+            "host": {"cpu_model": model, "usable_cores": avail}}
 
 
 def main():
@@ -210,6 +254,10 @@ def main():
     ap.add_argument("--block-size", type=int, default=None,
                     help="llama7b: block size (8/16/32/64) for the block-size trade-off; default 16")
     ap.add_argument("--copy-probe-gib", type=float, default=1.0, help="size of the plain-copy bandwidth probe")
+    ap.add_argument("--evict-mib", type=int, default=1024,
+                    help="MiB read (or written) before every step of the cold-cache pass (evicts L2 and MALL)")
+    ap.add_argument("--evict-mode", choices=["read", "write"], default="read",
+                    help="how the cold-cache pass evicts: read the scratch buffer (caches left clean) or write it")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="store HBM bytes per launch from two rocprofv3 --pmc runs of this script and exit")
     args = ap.parse_args()
@@ -297,6 +345,8 @@ def main():
         kv = unique_kv_bytes(d.block_tables, d.context_lens, H, D, elt, bs)  # each aliased byte once
         if shared:
             k2_bytes = kv + table + qo  # the whole shared-prefix call: distinct K/V, table, q and out
+        else:
+            k2_bytes -= logical_kv - kv  # the plain decode too is held to the distinct bytes
     step_bytes = kv + table + qo + cache_write_bytes + pf_bytes
 
     # eager pass: HIP events on the launch stream around every kernel launch
@@ -317,6 +367,30 @@ def main():
     cw_ms, pf_ms, k2_ms, k3_ms = phase_ms(0, 1), phase_ms(1, 2), phase_ms(2, 3), phase_ms(3, 4)
     eager_out = out.clone()
     eager_pf = pf_out.clone() if pf_out is not None else None
+
+    # cold pass: before every step 1 GiB of scratch is read (or written),
+    # outside the events, which evicts L2 and the memory-side cache, so each
+    # step reads its K/V from HBM. Reading leaves the caches clean; writing
+    # also leaves them full of dirty lines whose write-back the step pays for.
+    scratch = torch.zeros((args.evict_mib << 20) // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros((), dtype=torch.float32, device="cuda")
+    cold = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        if args.evict_mode == "read":
+            torch.sum(scratch, dim=0, out=sink)  # one reduction kernel that reads the buffer once
+        else:
+            scratch.fill_(float(i))
+        step(cold[i])
+    torch.cuda.synchronize()
+    del scratch, sink
+    cold_k2 = np.array([e[2].elapsed_time(e[3]) for e in cold])
+    cold_step = np.array([e[0].elapsed_time(e[4]) for e in cold])
+    if not torch.equal(out, eager_out):
+        raise SystemExit("cold-cache step output differs from the warm one")
+
+    def pct(x):
+        return {"mean": round(float(x.mean()) * 1e3, 2), "median": round(float(np.median(x)) * 1e3, 2),
+                "p10": round(float(np.percentile(x, 10)) * 1e3, 2), "p90": round(float(np.percentile(x, 90)) * 1e3, 2)}
 
     # the mixed step as one scheduler iteration: pa_attention_step with the
     # prefill on a side stream, concurrent with the decode
@@ -376,11 +450,14 @@ def main():
         else:
             ms_per_step, graph_ok = time_graph(step)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    k2_gbps = k2_bytes / (k2_ms * 1e-3) / 1e9
+    k2_cold_ms = float(cold_k2.mean())
+    k2_gbps = k2_bytes / (k2_cold_ms * 1e-3) / 1e9
+    k2_warm_gbps = k2_bytes / (k2_ms * 1e-3) / 1e9
     log(f"[bench] {ms_per_step * 1e3:.1f} us/step ({'graph' if not args.eager else 'eager'}; eager "
         f"{eager_ms * 1e3:.1f} us): cache write {cw_ms * 1e3:.1f} us"
         + (f", prefill {pf_ms * 1e3:.1f} us ({pf_flops / (pf_ms * 1e-3) / 1e12:.0f} TFLOP/s)" if p else "")
-        + f", partition kernel {k2_ms * 1e3:.1f} us ({k2_gbps:.0f} GB/s), reduction {k3_ms * 1e3:.1f} us, "
+        + f", partition kernel {k2_ms * 1e3:.1f} us warm ({k2_warm_gbps:.0f} GB/s), {k2_cold_ms * 1e3:.1f} us "
+          f"cold ({k2_gbps:.0f} GB/s), reduction {k3_ms * 1e3:.1f} us, "
           f"graph output == eager: {graph_ok}")
     if graph_ok is False:
         raise SystemExit("graph replay disagrees with the eager step")
@@ -410,7 +487,13 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, max(1, min(16, os.cpu_count() or 1)), kv + table + qo + pf_bytes)
+        def sample_bytes(rows):
+            kv_r, table_r, qo_r = decode_bytes(d.context_lens[:rows], H, D, elt, bs)
+            if args.workload == "prefix13b":
+                kv_r = unique_kv_bytes(d.block_tables[:rows], d.context_lens[:rows], H, D, elt, bs)
+            return kv_r + table_r + qo_r
+
+        cpu = cpu_baseline(wl, max(1, min(16, _host_cpu()[1])), kv + table + qo + pf_bytes, sample_bytes)
 
     rec = {
         "metric": METRIC if args.workload == "llama7b" else METRIC_OTHER,
@@ -432,10 +515,15 @@ def main():
                      "frac": round(k2_gbps / HBM_PEAK_GBPS, 4), "traffic": None if shared else traffic,
                      "kernel": ("shared-prefix decode call (shared, tail and reduction kernels)" if shared
                                 else f"decode_partition_kernel<{wl.dtype},{D},{bs}>"),
-                     "bytes_per_launch": k2_bytes, "avg_launch_us": round(k2_ms * 1e3, 2)},
+                     "bytes_per_launch": k2_bytes, "avg_launch_us": round(k2_cold_ms * 1e3, 2),
+                     "timing": f"HIP events on the launch stream around each of {args.steps} eager launches, "
+                               f"each after a {args.evict_mib} MiB {args.evict_mode} that evicts L2 and MALL",
+                     "launch_us": pct(cold_k2), "warm_avg_launch_us": round(k2_ms * 1e3, 2),
+                     "warm_GBps": round(k2_warm_gbps, 1)},
         "timing": ("hip_graph_replay" + (" of pa_attention_step (prefill on a side stream, concurrent with the "
                                           "decode)" if p is not None else "")) if not args.eager else "eager",
         "eager_ms_per_step": round(eager_ms, 5),
+        "cold_step_us": pct(cold_step),
         "hbm_copy_probe_GBps": round(copy_gbps, 1),
         "step_bytes": step_bytes,
         "phases_us": {"reshape_and_cache": round(cw_ms * 1e3, 2), "decode_partitions": round(k2_ms * 1e3, 2),
@@ -450,8 +538,8 @@ def main():
     if args.workload == "prefix13b":
         rec["aliasing"] = {"path": "shared-prefix decode" if shared else "plain decode",
                            "logical_kv_bytes": logical_kv, "unique_kv_bytes": kv,
-                           "logical_GBps": round(logical_kv / (k2_ms * 1e-3) / 1e9, 1),
-                           "unique_GBps": round(kv / (k2_ms * 1e-3) / 1e9, 1)}
+                           "logical_GBps": round(logical_kv / (k2_cold_ms * 1e-3) / 1e9, 1),
+                           "unique_GBps": round(kv / (k2_cold_ms * 1e-3) / 1e9, 1)}
     if p is not None:
         pf_tflops = pf_flops / (pf_ms * 1e-3) / 1e12
         rec["phases_us"]["prefill"] = round(pf_ms * 1e3, 2)
