@@ -342,7 +342,9 @@ static pa_status prepare_prefill(PrefillCall& call, void* out, pa_dtype out_dtyp
     a.max_blocks = max_blocks_per_seq;
     a.max_context_len = max_context_len;
     a.q_tiles = (int)ceil_div(max_q_len, pa::prefill_mfma_q_tile());
-    a.scale_log2 = scale_log2;
+    // a negative scale runs as |scale| on negated queries (a sign flip, exact)
+    a.scale_log2 = std::fabs(scale) * 1.4426950408889634f;
+    a.q_sign = std::signbit(scale) ? 0x80008000u : 0u;
     a.out_f32 = out_dtype == PA_F32 ? 1 : 0;
     if ((int64_t)a.q_tiles * num_heads * num_seqs > INT32_MAX) return PA_ERR_INVALID_ARG;
     return PA_OK;

@@ -111,6 +111,25 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+// Max / sum over the four 16-lane rows of the wave (lanes i, i^16, i^32,
+// i^48), on the gfx950 row-swap instructions: with both operands holding x,
+// v_permlane16_swap leaves x and its xor-16 partner in the two results (in
+// one order or the other, which max and + do not mind), v_permlane32_swap
+// does the same for the xor-32 partner. VALU only, no LDS round trip; the
+// sum adds in the order (x0 + x16) + (x32 + x48). Every lane must be active.
+__device__ __forceinline__ float rows4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x), false, false);
+  x = fmaxf(__builtin_bit_cast(float, (int)a[0]), __builtin_bit_cast(float, (int)a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (int)b[0]), __builtin_bit_cast(float, (int)b[1]));
+}
+__device__ __forceinline__ float rows4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x), false, false);
+  x = __builtin_bit_cast(float, (int)a[0]) + __builtin_bit_cast(float, (int)a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x), false, false);
+  return __builtin_bit_cast(float, (int)b[0]) + __builtin_bit_cast(float, (int)b[1]);
+}
+
 // xor shuffle across the whole wave (through ds_bpermute)
 __device__ __forceinline__ float shfl_xor_f(float x, int m) {
   int lane = __lane_id();

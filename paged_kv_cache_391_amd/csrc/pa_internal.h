@@ -112,7 +112,8 @@ struct PrefillArgs {
   int max_blocks;
   int max_context_len;
   int q_tiles;                      // grid: q tiles per sequence
-  float scale_log2;
+  float scale_log2;                 // |scale| * log2(e)
+  uint32_t q_sign;                  // 0x80008000 for a negative scale (queries negated), else 0
   int out_f32;
 };
 hipError_t launch_prefill_mfma(const PrefillArgs& a, Dt dt, int D, int BS, hipStream_t stream);

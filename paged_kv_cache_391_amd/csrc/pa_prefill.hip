@@ -13,21 +13,28 @@
 // score accumulator a lane holds (one query, four keys per 16-key subtile)
 // is exactly the B operand P^T needs, so P never leaves registers; the
 // price is a transposed V tile, which the workgroup writes into LDS while
-// staging it. Per tile of KT keys (32 or 64):
-//   * the workgroup keeps a window of the sequence's block-table row in
-//     LDS; 256 threads gather each K tile (row-major) and V tile
-//     (transposed) through it into one of two LDS buffers. Tile t+2's
+// staging it. Per tile of KT keys:
+//   * addressing is scalar: every global load of a wave covers a few
+//     consecutive keys that lie in one block, so the wave reads the block's
+//     id with a scalar load (the scalar cache keeps the table row), forms
+//     the row address in scalar registers and adds only a fixed per-lane
+//     offset;
+//   * 256 threads gather each K tile (row-major) and V tile (transposed,
+//     key pairs packed with v_perm) into one of two LDS buffers; tile t+R's
 //     global loads are in flight while tile t is computed and tile t+1 is
-//     staged, one barrier per tile;
+//     staged, one barrier per tile; only the last tile clamps and zeroes;
 //   * each wave owns NQ groups of 16 queries; every K or V^T fragment read
 //     from LDS feeds one MFMA per group;
-//   * online softmax per query: in-lane max/sum over the lane's keys plus
-//     two cross-row shuffles; only tiles that cross a wave's first query
-//     carry the causal mask, tiles past its last query are skipped, and the
-//     running max is raised lazily (see compute()) so the accumulators are
-//     rescaled only on the few tiles that need it.
+//   * online softmax per query: the max over the raw scores (the scale is
+//     applied once to it, and inside the exponent's FMA), cross-row max and
+//     sum on the row-swap instructions; only tiles that cross a wave's first
+//     query carry the causal mask, tiles past its last query are skipped,
+//     and the running max is raised lazily (see compute()) so the
+//     accumulators are rescaled only on the few tiles that need it.
 // P is rounded to the input type for the P.V product; for bf16 it is split
-// into a bf16 head and a bf16 remainder (two MFMAs) to keep ~16 bits.
+// into a bf16 head and a bf16 remainder (two MFMAs) to keep ~16 bits. A
+// negative scale is applied as |scale| on negated queries (exact: a sign
+// flip), so the max of the raw scores is the max of the scaled ones.
 #include "pa_internal.h"
 
 namespace pa {
@@ -40,11 +47,15 @@ namespace {
 #ifndef PA_PREFILL_NQ
 #define PA_PREFILL_NQ 2
 #endif
+#ifndef PA_PREFILL_R
+#define PA_PREFILL_R 2
+#endif
 constexpr int KT = PA_PREFILL_KT;  // keys per tile (32 or 64)
 constexpr int NQ = PA_PREFILL_NQ;  // 16-query groups per wave
 constexpr int QW = 16 * NQ;        // queries per wave
 constexpr int QT = 4 * QW;         // queries per workgroup
-constexpr int MAXB_LDS = 256;      // block-table entries staged in LDS (a sliding window)
+constexpr int R = PA_PREFILL_R;    // register sets: tile t+R is fetched while tile t is computed
+constexpr int UNR = R % 2 == 0 ? R : 2 * R;  // loop unroll: a multiple of R and of the two LDS buffers
 constexpr float RESCALE_LOG2 = 8.f; // lazy rescale threshold (log2 units): p < 256 between rescales
 static_assert(KT == 32 || KT == 64, "key tile must be 32 or 64");
 
@@ -57,16 +68,23 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
   constexpr int NSUB = KT / 16;  // 16-key subtiles of S^T
   constexpr int NKST = KT / 32;  // MFMA k-steps over keys for P.V
   constexpr int CPR = D / 8;     // 16-byte chunks per K/V row
+  constexpr int ROWB = D * 2;    // bytes per K/V row
   constexpr int KROW = D + 8;    // K tile row stride in LDS (halves), padded against bank conflicts
   constexpr int VROW = KT + 4;   // V^T tile row stride in LDS (halves)
   constexpr int NKC = KT * CPR;          // K chunks per tile
   constexpr int NVP = (KT / 2) * CPR;    // V (key pair, chunk) items per tile
-  constexpr int KCH = (NKC + 255) / 256;
+  constexpr int KCH = NKC / 256;
   constexpr int VPR = (NVP + 255) / 256;
+  // one load of a wave covers KW consecutive keys of K, VW of V (in pairs)
+  constexpr int KW = 64 / CPR;
+  constexpr int VW = 2 * 64 / CPR;
+  constexpr bool V_ONE_BLOCK = VW <= BS;
+  static_assert(NKC % 256 == 0, "whole K chunks per thread");
+  static_assert(KW <= BS && BS % KW == 0, "a wave's K rows of one load lie in one block");
+  static_assert(V_ONE_BLOCK || VW == 2 * BS, "a wave's V rows of one load span at most two blocks");
 
   __shared__ __align__(16) uint16_t sk[2][KT * KROW];
   __shared__ __align__(16) uint16_t sv[2][D * VROW];
-  __shared__ int32_t sbt[MAXB_LDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -95,12 +113,9 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
   const char* kc = reinterpret_cast<const char*>(a.k_cache);
   const char* vc = reinterpret_cast<const char*>(a.v_cache);
   const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks;
-
-  // the table entries this workgroup reads sit in LDS: a window of
-  // MAXB_LDS entries starting at w0, moved forward when a tile leaves it
-  const int nb_needed = (kv_end + BS - 1) / BS;
-  int w0 = 0;
-  for (int i = tid; i < min(nb_needed, MAXB_LDS); i += 256) sbt[i] = bt_row[i];
+  const int nb = (kv_end + BS - 1) / BS;           // blocks this workgroup reads
+  const int64_t blk_bytes = (int64_t)a.H * BS * ROWB;
+  const int64_t head_bytes = (int64_t)h * BS * ROWB;
 
   // Q^T fragments (B operand of S^T = K Q^T): query n16 of group g, d = 32*ks + 8*g4 .. +7
   u32x4 qf[NQ][KS];
@@ -111,7 +126,8 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
     for (int ks = 0; ks < KS; ++ks) {
       if (jq < L) {
         const char* p = reinterpret_cast<const char*>(a.q) + (((int64_t)(q_beg + jq) * a.H + h) * D + ks * 32 + 8 * g4) * 2;
-        qf[g][ks] = *reinterpret_cast<const u32x4*>(p);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+        qf[g][ks] = u32x4{v[0] ^ a.q_sign, v[1] ^ a.q_sign, v[2] ^ a.q_sign, v[3] ^ a.q_sign};
       } else {
         qf[g][ks] = u32x4{0u, 0u, 0u, 0u};
       }
@@ -128,78 +144,84 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
     for (int dt = 0; dt < NDT; ++dt) o[g][dt] = zero4();
   }
 
-  __syncthreads();  // block table visible
-  auto block_of = [&](int pos) -> int32_t { return sbt[pos / BS - w0]; };
-  // make the window cover tile t (uniform across the workgroup; called where
-  // no thread is reading the window)
-  auto window_for = [&](int t) {
-    const int last = (min((t + 1) * KT, kv_end) - 1) / BS;
-    if (last >= w0 + MAXB_LDS) {
-      __syncthreads();
-      w0 = (t * KT) / BS;
-      for (int i = tid; i < min(nb_needed - w0, MAXB_LDS); i += 256) sbt[i] = bt_row[w0 + i];
-      __syncthreads();
-    }
+  // wave-uniform address of row `key` (tile-absolute) of head h, its block
+  // id read through the scalar cache; keys past the sequence's blocks read
+  // the last block's rows (zeroed when staged)
+  auto row_base = [&](const char* cache, int key) -> const char* {
+    const int blk = min(key / BS, nb - 1);
+    const int32_t phys = bt_row[blk];
+    return cache + (int64_t)phys * blk_bytes + head_bytes + (int64_t)(key % BS) * ROWB;
   };
+  // per-lane byte offsets inside a wave's rows of one load
+  const uint32_t k_lane = lane * 16;
+  uint32_t v_lane[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+    v_lane[e] = ((2 * (lane / CPR) + e) % (V_ONE_BLOCK ? VW : BS)) * ROWB + (lane % CPR) * 16;
 
   // ---- global -> registers for one tile. Every load is issued
-  // unconditionally (positions clamped into [0, kv_end), lanes past the tile
-  // clamped onto its last chunk), so all of a tile's loads are in flight
-  // together; rows past kv_end are zeroed when the tile is staged.
-  u32x4 kreg_a[KCH], vreg_a[2 * VPR], kreg_b[KCH], vreg_b[2 * VPR];
-  auto fetch = [&](u32x4 (&kreg)[KCH], u32x4 (&vreg)[2 * VPR], int t) {
-    window_for(t);
+  // unconditionally, so all of a tile's loads are in flight together.
+  u32x4 kreg[R][KCH], vreg[R][2 * VPR];
+  auto fetch = [&](u32x4 (&kr)[KCH], u32x4 (&vr)[2 * VPR], int t) {
     const int kv0 = t * KT;
 #pragma unroll
     for (int r = 0; r < KCH; ++r) {
-      const int ci = min(tid + 256 * r, NKC - 1);
-      const int key = ci / CPR, dc = ci % CPR;
-      const int pos = min(kv0 + key, kv_end - 1);
-      kreg[r] = *reinterpret_cast<const u32x4*>(kc + kv_row_offset(block_of(pos), h, pos % BS, a.H, BS, D) * 2 +
-                                                dc * 16);
+      const int key = kv0 + (wave * 64 + 256 * r) / CPR;
+      kr[r] = *reinterpret_cast<const u32x4*>(row_base(kc, key) + k_lane);
     }
 #pragma unroll
     for (int r = 0; r < VPR; ++r) {
-      const int pi = min(tid + 256 * r, NVP - 1);
-      const int kp = pi / CPR, dc = pi % CPR;
+      const int pw = min(wave * 64 + 256 * r, NVP - 64);  // waves past the tile's pairs repeat the last ones
+      const int key = kv0 + 2 * (pw / CPR);
+      if constexpr (V_ONE_BLOCK) {
+        const char* base = row_base(vc, key);
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int pos = min(kv0 + 2 * kp + e, kv_end - 1);
-        vreg[2 * r + e] = *reinterpret_cast<const u32x4*>(
-            vc + kv_row_offset(block_of(pos), h, pos % BS, a.H, BS, D) * 2 + dc * 16);
+        for (int e = 0; e < 2; ++e) vr[2 * r + e] = *reinterpret_cast<const u32x4*>(base + v_lane[e]);
+      } else {  // lanes 0..31 read the first block, 32..63 the next
+        const char* b0 = row_base(vc, key);
+        const char* b1 = row_base(vc, key + BS);
+        const char* base = lane < 32 ? b0 : b1;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) vr[2 * r + e] = *reinterpret_cast<const u32x4*>(base + v_lane[e]);
       }
     }
   };
-  // ---- registers -> LDS buffer b: K row-major, V transposed (two keys packed per word)
-  auto stage = [&](int b, int t, const u32x4 (&kreg)[KCH], const u32x4 (&vreg)[2 * VPR]) {
+  // ---- registers -> LDS buffer b: K row-major, V transposed (two keys
+  // packed per word); rows at or past kv_end (last tile only) become zeros
+  auto stage = [&](int b, int t, const u32x4 (&kr)[KCH], const u32x4 (&vr)[2 * VPR]) {
     const int kv0 = t * KT;
-    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+    auto put = [&](bool tail) {
+      const u32x4 z = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int r = 0; r < KCH; ++r) {
-      const int ci = tid + 256 * r;
-      if (NKC % 256 == 0 || ci < NKC) {
-        const int key = ci / CPR, dc = ci % CPR;
-        *reinterpret_cast<u32x4*>(&sk[b][key * KROW + dc * 8]) = kv0 + key < kv_end ? kreg[r] : z;
+      for (int r = 0; r < KCH; ++r) {
+        const int key = (wave * 64 + 256 * r) / CPR + lane / CPR;
+        const int dc = lane % CPR;
+        *reinterpret_cast<u32x4*>(&sk[b][key * KROW + dc * 8]) = (tail && kv0 + key >= kv_end) ? z : kr[r];
       }
-    }
 #pragma unroll
-    for (int r = 0; r < VPR; ++r) {
-      const int pi = tid + 256 * r;
-      if (NVP % 256 == 0 || pi < NVP) {
-        const int kp = pi / CPR, dc = pi % CPR;
-        const u32x4 v0 = kv0 + 2 * kp < kv_end ? vreg[2 * r] : z;
-        const u32x4 v1 = kv0 + 2 * kp + 1 < kv_end ? vreg[2 * r + 1] : z;
+      for (int r = 0; r < VPR; ++r) {
+        const int pw = wave * 64 + 256 * r;
+        if (NVP % 256 == 0 || pw < NVP) {
+          const int kp = pw / CPR + lane / CPR;
+          const int dc = lane % CPR;
+          const u32x4 v0 = (tail && kv0 + 2 * kp >= kv_end) ? z : vr[2 * r];
+          const u32x4 v1 = (tail && kv0 + 2 * kp + 1 >= kv_end) ? z : vr[2 * r + 1];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t lo = (v0[w] & 0xffffu) | (v1[w] << 16);      // element 2w of keys 2kp, 2kp+1
-          const uint32_t hi = (v0[w] >> 16) | (v1[w] & 0xffff0000u);  // element 2w+1
-          *reinterpret_cast<uint32_t*>(&sv[b][(dc * 8 + 2 * w) * VROW + 2 * kp]) = lo;
-          *reinterpret_cast<uint32_t*>(&sv[b][(dc * 8 + 2 * w + 1) * VROW + 2 * kp]) = hi;
+          for (int w = 0; w < 4; ++w) {
+            // element 2w of keys 2kp, 2kp+1 (low halves), then element 2w+1 (high halves)
+            const uint32_t lo = __builtin_amdgcn_perm(v1[w], v0[w], 0x05040100u);
+            const uint32_t hi = __builtin_amdgcn_perm(v1[w], v0[w], 0x07060302u);
+            *reinterpret_cast<uint32_t*>(&sv[b][(dc * 8 + 2 * w) * VROW + 2 * kp]) = lo;
+            *reinterpret_cast<uint32_t*>(&sv[b][(dc * 8 + 2 * w + 1) * VROW + 2 * kp]) = hi;
+          }
         }
       }
-    }
+    };
+    if (kv0 + KT > kv_end) put(true);
+    else put(false);
   };
 
+  const float c = a.scale_log2;  // >= 0
   auto compute = [&](int b, int kv0) {
     // S^T = K Q^T over NSUB key subtiles of 16
     f32x4 sacc[NQ][NSUB];
@@ -231,18 +253,24 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
       const int qpos = c0 + wq0 + g * 16 + n16;
       const int last_key = min(qpos, kv_end - 1);
       float sc[4 * NSUB];
-      float mt = -INFINITY;
+      bool ok[4 * NSUB];
 #pragma unroll
       for (int sub = 0; sub < NSUB; ++sub)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int key = kv0 + 16 * sub + 4 * g4 + i;
-          const float x = sacc[g][sub][i] * a.scale_log2;
-          sc[4 * sub + i] = (!masked || key <= last_key) ? x : -INFINITY;
-          mt = fmaxf(mt, sc[4 * sub + i]);
+          ok[4 * sub + i] = !masked || kv0 + 16 * sub + 4 * g4 + i <= last_key;
+          sc[4 * sub + i] = sacc[g][sub][i];
         }
-      mt = fmaxf(mt, shfl_xor_f(mt, 16));
-      mt = fmaxf(mt, shfl_xor_f(mt, 32));
+      float mr = -INFINITY;  // max of the raw scores of the lane's allowed keys
+      if (masked) {
+#pragma unroll
+        for (int i = 0; i < 4 * NSUB; ++i) mr = fmaxf(mr, ok[i] ? sc[i] : -INFINITY);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4 * NSUB; ++i) mr = fmaxf(mr, sc[i]);
+      }
+      mr = rows4_max(mr);
+      const float mt = mr == -INFINITY ? -INFINITY : mr * c;  // c >= 0: max of the scaled scores
       const bool grow = mt > m[g] + RESCALE_LOG2;  // also true for the first tile (m = -inf)
       if (__any(grow)) {
         const float m_new = grow ? mt : m[g];
@@ -252,12 +280,13 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
         for (int dt = 0; dt < NDT; ++dt) o[g][dt] *= alpha;
         m[g] = m_new;
       }
-      const float m_use = m[g] == -INFINITY ? 0.f : m[g];
+      const float neg_m = m[g] == -INFINITY ? 0.f : -m[g];
       float psum = 0.f;
       uint32_t ph[4 * NSUB], pl[4 * NSUB];
 #pragma unroll
       for (int i = 0; i < 4 * NSUB; ++i) {
-        const float p = __builtin_amdgcn_exp2f(sc[i] - m_use);
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c, neg_m));
+        if (masked) p = ok[i] ? p : 0.f;
         psum += p;
         ph[i] = to_bits<DT>(p);
         pl[i] = DT == Dt::BF16 ? to_bits<DT>(p - from_bits<DT>(ph[i])) : 0u;
@@ -292,35 +321,33 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
     }
   };
 
-  // Two LDS buffers and two register sets: tile t+2 travels global ->
-  // registers while tile t is computed and tile t+1 (fetched one iteration
-  // earlier) is staged into the other LDS buffer; one barrier per tile.
-  // Even tiles use LDS buffer 0 and register set a, odd tiles buffer 1 and
-  // set b. Fetches and stages are unconditional (past the end they re-read
-  // the last tile, an L2 hit, and stage zeros that are never read) so the
-  // compiler can prove each set's loads were consumed before it is
-  // refilled and never drains the load queue early.
-  fetch(kreg_a, vreg_a, 0);
-  fetch(kreg_b, vreg_b, min(1, n_tiles - 1));
-  stage(0, 0, kreg_a, vreg_a);
+  // R register sets in a ring and two LDS buffers: while tile t is
+  // computed, tile t+R travels global -> registers (set t % R) and tile t+1,
+  // fetched R-1 tiles earlier, is staged into the other LDS buffer; one
+  // barrier per tile. Fetches and stages are unconditional (past the end
+  // they re-read the last tile, an L2 hit, and stage zeros that are never
+  // read) so the compiler can prove each set's loads were consumed before it
+  // is refilled and never drains the load queue early.
+#pragma unroll
+  for (int r = 0; r < R; ++r) fetch(kreg[r], vreg[r], min(r, n_tiles - 1));
+  stage(0, 0, kreg[0], vreg[0]);
   __syncthreads();
-  for (int t = 0; t < n_tiles; t += 2) {
-    fetch(kreg_a, vreg_a, min(t + 2, n_tiles - 1));
-    if (wave_active && t * KT <= wave_last_pos) compute(0, t * KT);
-    stage(1, t + 1, kreg_b, vreg_b);
-    __syncthreads();
-    fetch(kreg_b, vreg_b, min(t + 3, n_tiles - 1));
-    if (wave_active && t + 1 < n_tiles && (t + 1) * KT <= wave_last_pos) compute(1, (t + 1) * KT);
-    stage(0, t + 2, kreg_a, vreg_a);
-    __syncthreads();
+  for (int t0 = 0; t0 < n_tiles; t0 += UNR) {
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int t = t0 + u;
+      fetch(kreg[u % R], vreg[u % R], min(t + R, n_tiles - 1));
+      if (wave_active && t < n_tiles && t * KT <= wave_last_pos) compute(u & 1, t * KT);
+      stage((u + 1) & 1, t + 1, kreg[(u + 1) % R], vreg[(u + 1) % R]);
+      __syncthreads();
+    }
   }
 
   if (!wave_active) return;
   // finish: l summed over the four lane rows that share a query
 #pragma unroll
   for (int g = 0; g < NQ; ++g) {
-    float lt = l[g] + shfl_xor_f(l[g], 16);
-    lt += shfl_xor_f(lt, 32);
+    const float lt = rows4_sum(l[g]);
     const int jq = wq0 + g * 16 + n16;
     if (jq >= L) continue;
     const int64_t orow = ((int64_t)(q_beg + jq) * a.H + h) * D;

@@ -172,8 +172,7 @@ __device__ __forceinline__ void shared_prefix_body(const DecodeArgs& a, int bid)
         x[4 * sb + i] = (!partial || key < k_end) ? v : -INFINITY;
         mt = fmaxf(mt, x[4 * sb + i]);
       }
-    mt = fmaxf(mt, shfl_xor_f(mt, 16));
-    mt = fmaxf(mt, shfl_xor_f(mt, 32));
+    mt = rows4_max(mt);
     const bool grow = mt > m + kRescaleLog2;  // true on the first step (m = -inf)
     if (__any(grow)) {
       const float m_new = grow ? mt : m;
@@ -229,8 +228,7 @@ __device__ __forceinline__ void shared_prefix_body(const DecodeArgs& a, int bid)
   }
 
   // merge the four lane rows of each member; write the partial or output
-  float lt = l + shfl_xor_f(l, 16);
-  lt += shfl_xor_f(lt, 32);
+  const float lt = rows4_sum(l);
   if (n16 >= nm) return;
   const int row = m0 + n16;
   const int ctx = a.context_lens[row];

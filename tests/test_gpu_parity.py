@@ -375,12 +375,48 @@ def test_prefill_parity_small_chunks(dtype, bs):
         assert np.array_equal(bits(host(outn)), bits(rne(host(out32), dtype)))
 
 
+@pytest.mark.parametrize("dtype,bs", [("f16", 8), ("bf16", 16), ("f16", 64)])
+def test_prefill_head_dim_64(dtype, bs):
+    """head_dim 64: a wave's V rows of one load span two 8-token blocks at
+    block size 8 (the kernel's per-lane block choice)."""
+    prior = [0, 9, 40, 250]
+    chunk = [3, 70, 129, 33]
+    maxb = math.ceil(max(p + c for p, c in zip(prior, chunk)) / bs)
+    wl = prefill_workload(f"pf64_{dtype}_{bs}", 760 + bs, dtype, 3, 64, bs, prior, chunk, maxb=maxb, pool_factor=1.3)
+    od = _on_device_written(wl)
+    kc, vc = oracle.reshape_and_cache(wl.new.k, wl.new.v, wl.k_cache, wl.v_cache, wl.new.slot_mapping, bs, dtype)
+    p = wl.prefill
+    ref = oracle.prefill(p.q, kc, vc, p.block_tables, p.context_lens, p.query_start_loc, wl.scale, dtype)
+    got = host(od.prefill(torch.float32)).astype(np.float64)
+    err = np.abs(got - ref).max()
+    assert err <= ATOL[dtype], f"prefill max abs err {err:.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("scale", [-0.2, 0.0])
+def test_prefill_negative_and_zero_scale(dtype, scale):
+    """A negative scale (run as |scale| on sign-flipped queries) and a zero
+    scale (every allowed key weighs the same; the causal mask still holds)."""
+    prior, chunk = [0, 60, 200], [40, 100, 17]
+    maxb = math.ceil(max(p + c for p, c in zip(prior, chunk)) / 16)
+    wl = prefill_workload(f"pf_scale_{dtype}_{scale}", 770, dtype, 2, 128, 16, prior, chunk, maxb=maxb,
+                          pool_factor=1.2, scale=scale)
+    od = _on_device_written(wl)
+    kc, vc = oracle.reshape_and_cache(wl.new.k, wl.new.v, wl.k_cache, wl.v_cache, wl.new.slot_mapping, 16, dtype)
+    p = wl.prefill
+    ref = oracle.prefill(p.q, kc, vc, p.block_tables, p.context_lens, p.query_start_loc, wl.scale, dtype)
+    got = host(od.prefill(torch.float32)).astype(np.float64)
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref).max()
+    assert err <= ATOL[dtype], f"prefill max abs err {err:.3e}"
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("scale", [None, 1.0])
 def test_prefill_long_context_and_wide_scores(dtype, scale):
-    """Contexts past 256 blocks (the kernel's block-table window moves) and,
-    with scale 1, scores spread over hundreds of log2 units (the running max
-    is raised and the accumulators rescaled many times)."""
+    """Contexts of hundreds of blocks (block ids read far into the table row)
+    and, with scale 1, scores spread over hundreds of log2 units (the running
+    max is raised and the accumulators rescaled many times)."""
     prior, chunk = [4500, 8200, 0], [70, 150, 90]
     maxb = math.ceil(max(p + c for p, c in zip(prior, chunk)) / 16)
     wl = prefill_workload(f"pf_long_{dtype}", 705, dtype, 2, 128, 16, prior, chunk, maxb=maxb, pool_factor=1.1,
