@@ -83,6 +83,16 @@ template <Dt DT> __device__ __forceinline__ float from_bits(uint32_t b) {
   else return bf16_bits_to_f32(b);
 }
 
+// Two floats narrowed into one word of two 16-bit values (lo in bits 0..15),
+// round to nearest even, on the packed v_cvt_pk_{f16,bf16}_f32 converts.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+template <Dt DT> __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (DT == Dt::F16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, half2_t));
+  else return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf162_t));
+}
+// 1.0 in both halves of a word, in the input type
+template <Dt DT> constexpr uint32_t ones2() { return DT == Dt::F16 ? 0x3C003C00u : 0x3F803F80u; }
+
 // ---- paged address translation ---------------------------------------------
 // Caches are [num_blocks][H][BS][D]. Logical token t of a sequence lives in
 // physical block table[t / BS] at offset t % BS; one (block, head) tile of

@@ -26,11 +26,13 @@
 //   * each wave owns NQ groups of 16 queries; every K or V^T fragment read
 //     from LDS feeds one MFMA per group;
 //   * online softmax per query: the max over the raw scores (the scale is
-//     applied once to it, and inside the exponent's FMA), cross-row max and
-//     sum on the row-swap instructions; only tiles that cross a wave's first
-//     query carry the causal mask, tiles past its last query are skipped,
-//     and the running max is raised lazily (see compute()) so the
-//     accumulators are rescaled only on the few tiles that need it.
+//     applied once to it, and inside the exponent's FMA), cross-row max on
+//     the row-swap instructions, P narrowed with the packed converts; the
+//     denominator is summed on the matrix cores (a block of ones in V^T);
+//     only tiles that cross a wave's first query carry the causal mask (the
+//     masked scores are set to -inf), tiles past its last query are skipped, and
+//     the running max is raised lazily (see compute()) so the accumulators
+//     are rescaled only on the few tiles that need it.
 // P is rounded to the input type for the P.V product; for bf16 it is split
 // into a bf16 head and a bf16 remainder (two MFMAs) to keep ~16 bits. A
 // negative scale is applied as |scale| on negated queries (exact: a sign
@@ -114,8 +116,8 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
   const char* vc = reinterpret_cast<const char*>(a.v_cache);
   const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks;
   const int nb = (kv_end + BS - 1) / BS;           // blocks this workgroup reads
-  const int64_t blk_bytes = (int64_t)a.H * BS * ROWB;
-  const int64_t head_bytes = (int64_t)h * BS * ROWB;
+  const uint32_t blk_bytes = (uint32_t)a.H * BS * ROWB;   // one block of every head (< 2^32)
+  const uint32_t head_bytes = (uint32_t)h * BS * ROWB;
 
   // Q^T fragments (B operand of S^T = K Q^T): query n16 of group g, d = 32*ks + 8*g4 .. +7
   u32x4 qf[NQ][KS];
@@ -134,23 +136,29 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
     }
   }
 
-  f32x4 o[NQ][NDT];
-  float m[NQ], l[NQ];
+  // o: O^T of the wave's queries; lacc: the softmax denominators, summed on
+  // the matrix cores as a 17th row block of ones in V^T (every row of lacc
+  // holds the sum of the query's rounded P, the same P the numerator uses)
+  f32x4 o[NQ][NDT], lacc[NQ];
+  float m[NQ];
 #pragma unroll
   for (int g = 0; g < NQ; ++g) {
     m[g] = -INFINITY;
-    l[g] = 0.f;
+    lacc[g] = zero4();
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[g][dt] = zero4();
   }
+  constexpr uint32_t ONE2 = ones2<DT>();
+  const u32x4 ones = u32x4{ONE2, ONE2, ONE2, ONE2};
 
   // wave-uniform address of row `key` (tile-absolute) of head h, its block
   // id read through the scalar cache; keys past the sequence's blocks read
   // the last block's rows (zeroed when staged)
   auto row_base = [&](const char* cache, int key) -> const char* {
-    const int blk = min(key / BS, nb - 1);
-    const int32_t phys = bt_row[blk];
-    return cache + (int64_t)phys * blk_bytes + head_bytes + (int64_t)(key % BS) * ROWB;
+    const uint32_t k = (uint32_t)key;
+    const uint32_t blk = min(k / BS, (uint32_t)(nb - 1));
+    const uint32_t phys = (uint32_t)bt_row[blk];
+    return cache + ((uint64_t)phys * blk_bytes + (head_bytes + (k % BS) * ROWB));
   };
   // per-lane byte offsets inside a wave's rows of one load
   const uint32_t k_lane = lane * 16;
@@ -221,7 +229,10 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
     else put(false);
   };
 
-  const float c = a.scale_log2;  // >= 0
+  // |scale| * log2(e), floored at the smallest normal float so that a
+  // masked score (-inf) times c stays -inf: a zero scale then weighs every
+  // allowed key equally to within 1e-26
+  const float c = fmaxf(a.scale_log2, 1.17549435e-38f);
   auto compute = [&](int b, int kv0) {
     // S^T = K Q^T over NSUB key subtiles of 16
     f32x4 sacc[NQ][NSUB];
@@ -246,61 +257,58 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
     // accumulators are rescaled only on the (rare) tiles where some row
     // needs it; the final O / l is the same softmax.
     const bool masked = kv0 + KT - 1 > c0 + wq0;
+    if (masked) {  // keys past a query's position score -inf
+#pragma unroll
+      for (int g = 0; g < NQ; ++g) {
+        const int last_key = min(c0 + wq0 + g * 16 + n16, kv_end - 1);
+#pragma unroll
+        for (int sub = 0; sub < NSUB; ++sub)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (kv0 + 16 * sub + 4 * g4 + i > last_key) sacc[g][sub][i] = -INFINITY;
+      }
+    }
     u32x4 pb[NQ][NKST];
     u32x4 pbl[NQ][NKST];  // bf16 remainders
 #pragma unroll
     for (int g = 0; g < NQ; ++g) {
-      const int qpos = c0 + wq0 + g * 16 + n16;
-      const int last_key = min(qpos, kv_end - 1);
-      float sc[4 * NSUB];
-      bool ok[4 * NSUB];
+      float mr = -INFINITY;  // max of the raw scores (c > 0: the scaled max is mr * c)
 #pragma unroll
       for (int sub = 0; sub < NSUB; ++sub)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ok[4 * sub + i] = !masked || kv0 + 16 * sub + 4 * g4 + i <= last_key;
-          sc[4 * sub + i] = sacc[g][sub][i];
-        }
-      float mr = -INFINITY;  // max of the raw scores of the lane's allowed keys
-      if (masked) {
-#pragma unroll
-        for (int i = 0; i < 4 * NSUB; ++i) mr = fmaxf(mr, ok[i] ? sc[i] : -INFINITY);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4 * NSUB; ++i) mr = fmaxf(mr, sc[i]);
-      }
-      mr = rows4_max(mr);
-      const float mt = mr == -INFINITY ? -INFINITY : mr * c;  // c >= 0: max of the scaled scores
+        for (int i = 0; i < 4; ++i) mr = fmaxf(mr, sacc[g][sub][i]);
+      const float mt = rows4_max(mr) * c;
       const bool grow = mt > m[g] + RESCALE_LOG2;  // also true for the first tile (m = -inf)
       if (__any(grow)) {
         const float m_new = grow ? mt : m[g];
         const float alpha = __builtin_amdgcn_exp2f(m[g] - m_new);
-        l[g] *= alpha;
+        lacc[g] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o[g][dt] *= alpha;
         m[g] = m_new;
       }
       const float neg_m = m[g] == -INFINITY ? 0.f : -m[g];
-      float psum = 0.f;
-      uint32_t ph[4 * NSUB], pl[4 * NSUB];
+      float p[4 * NSUB];
 #pragma unroll
-      for (int i = 0; i < 4 * NSUB; ++i) {
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c, neg_m));
-        if (masked) p = ok[i] ? p : 0.f;
-        psum += p;
-        ph[i] = to_bits<DT>(p);
-        pl[i] = DT == Dt::BF16 ? to_bits<DT>(p - from_bits<DT>(ph[i])) : 0u;
-      }
-      l[g] += psum;
+      for (int sub = 0; sub < NSUB; ++sub)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[4 * sub + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[g][sub][i], c, neg_m));
       // B operand of O^T += V^T P^T for key step kst: elements 0..3 from
       // subtile 2*kst, 4..7 from subtile 2*kst+1
 #pragma unroll
       for (int kst = 0; kst < NKST; ++kst) {
-        const int b0 = 8 * kst;
-        pb[g][kst] = u32x4{ph[b0] | (ph[b0 + 1] << 16), ph[b0 + 2] | (ph[b0 + 3] << 16),
-                           ph[b0 + 4] | (ph[b0 + 5] << 16), ph[b0 + 6] | (ph[b0 + 7] << 16)};
-        pbl[g][kst] = u32x4{pl[b0] | (pl[b0 + 1] << 16), pl[b0 + 2] | (pl[b0 + 3] << 16),
-                            pl[b0 + 4] | (pl[b0 + 5] << 16), pl[b0 + 6] | (pl[b0 + 7] << 16)};
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = pack2<DT>(p[8 * kst + 2 * j], p[8 * kst + 2 * j + 1]);
+        pb[g][kst] = u32x4{w[0], w[1], w[2], w[3]};
+        if constexpr (DT == Dt::BF16) {
+          uint32_t r[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            r[j] = pack2<DT>(p[8 * kst + 2 * j] - __uint_as_float(w[j] << 16),
+                             p[8 * kst + 2 * j + 1] - __uint_as_float(w[j] & 0xffff0000u));
+          pbl[g][kst] = u32x4{r[0], r[1], r[2], r[3]};
+        }
       }
     }
     // O^T += V^T P^T: A = V^T rows d = 16*dt + n16, keys 32*kst + 4*g4 + {0..3} and +16
@@ -319,6 +327,13 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
         }
       }
     }
+#pragma unroll
+    for (int kst = 0; kst < NKST; ++kst)
+#pragma unroll
+      for (int g = 0; g < NQ; ++g) {
+        lacc[g] = mfma16<DT>(ones, pb[g][kst], lacc[g]);
+        if constexpr (DT == Dt::BF16) lacc[g] = mfma16<DT>(ones, pbl[g][kst], lacc[g]);
+      }
   };
 
   // R register sets in a ring and two LDS buffers: while tile t is
@@ -344,10 +359,10 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
   }
 
   if (!wave_active) return;
-  // finish: l summed over the four lane rows that share a query
+  // finish: every row of lacc holds the query's denominator
 #pragma unroll
   for (int g = 0; g < NQ; ++g) {
-    const float lt = rows4_sum(l[g]);
+    const float lt = lacc[g][0];
     const int jq = wq0 + g * 16 + n16;
     if (jq >= L) continue;
     const int64_t orow = ((int64_t)(q_beg + jq) * a.H + h) * D;
