@@ -163,20 +163,17 @@ __device__ __forceinline__ int group_of_row(const int32_t* group_starts, int num
   return lo;
 }
 
-// Partition layout of one row: the row's own tiles [tok0, ctx) are cut into
-// own = ceil(tiles / part_tiles) partitions of equal size (ptiles tiles, the
-// last one shorter by less than own), so a row never leaves a sliver of a
-// partition that finishes early while full ones start late; they sit in
-// workspace slots poff, poff+1, ... A row of a prefix-sharing group has
-// ceil(prefix / shared partition) shared partitions (written by the
-// shared-prefix kernel) in slots 0 .. poff-1.
+// Partition layout of one row: own partitions cover tokens [tok0, ctx) in
+// part_tiles-tile steps and sit in workspace slots poff, poff+1, ...; a row
+// of a prefix-sharing group has ceil(prefix / shared partition) shared
+// partitions (written by the shared-prefix kernel) in slots 0 .. poff-1.
 struct RowParts {
-  int tok0, own, poff, ptiles;
+  int tok0, own, poff;
   __device__ __forceinline__ int total() const { return poff + own; }
 };
 template <RowMode MODE>
 __device__ __forceinline__ RowParts row_parts(const DecodeArgs& a, int row, int ctx) {
-  RowParts rp{0, 0, 0, a.part_tiles};
+  RowParts rp{0, 0, 0};
   if constexpr (MODE == RowMode::SharedTail) {
     // the prefix is whole tiles inside the row (clamped so that a prefix
     // longer than the row can never send a read past the row's blocks)
@@ -187,7 +184,6 @@ __device__ __forceinline__ RowParts row_parts(const DecodeArgs& a, int row, int 
   }
   const int own_tiles = ((ctx + 15) >> 4) - (rp.tok0 >> 4);
   rp.own = (own_tiles + a.part_tiles - 1) / a.part_tiles;
-  if (rp.own > 1) rp.ptiles = (own_tiles + rp.own - 1) / rp.own;
   return rp;
 }
 
@@ -229,8 +225,8 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int b
   // tail of a shared prefix that covers the whole row
   if (part >= (rp.own > 0 ? rp.own : (rp.poff > 0 ? 0 : 1))) return;
 
-  const int u0 = (rp.tok0 >> 4) + part * rp.ptiles;
-  const int my_tiles = max(0, min(n_tiles, u0 + rp.ptiles) - u0);
+  const int u0 = (rp.tok0 >> 4) + part * a.part_tiles;
+  const int my_tiles = max(0, min(n_tiles, u0 + a.part_tiles) - u0);
 
   uint32_t qw[WPL];
   L::load(qw, reinterpret_cast<const char*>(a.q) + ((int64_t)row * a.H + h) * L::ROW_BYTES, (uint32_t)(c * L::VB));
