@@ -50,6 +50,7 @@ METRIC_OTHER = "paged attention step achieved HBM GB/s (% of peak)"
 HBM_PEAK_GBPS = 8000.0
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # dense fp16/bf16 matrix-core peak of MI355X
 KERNEL_SOURCES = ["pa_decode.hip", "pa_decode_device.h", "pa_device.h", "pa_internal.h"]
+SHARED_KERNEL_SOURCES = KERNEL_SOURCES + ["pa_shared.hip"]
 CPU_SECONDS = 10.0  # the oracle repeats its pass until about this much CPU time has elapsed
 
 WORKLOADS = {
@@ -65,13 +66,20 @@ WORKLOADS = {
 }
 
 
-def traffic_file(workload):
-    return os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
+def traffic_file(workload, shared=False):
+    tag = workload + ("_shared" if shared else "_plain" if workload == "prefix13b" else "")
+    return os.path.join(ROOT, "profiles", f"decode_{tag}_traffic.json")
 
 
-def kernel_source_hash():
+def traffic_kernel(shared):
+    """The kernel whose HBM traffic is recorded: the partition kernel, or the
+    shared-prefix step kernel for the shared-prefix call."""
+    return "shared_prefix_step_kernel" if shared else "decode_partition_kernel"
+
+
+def kernel_source_hash(shared=False):
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in (SHARED_KERNEL_SOURCES if shared else KERNEL_SOURCES):
         with open(os.path.join(ROOT, "paged_kv_cache_391_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -96,16 +104,17 @@ def _counter_rows(path):
     return rows
 
 
-def record_traffic(workload, fetch_dir, write_dir, copy_bytes):
+def record_traffic(workload, shared, fetch_dir, write_dir, copy_bytes):
     """Turn two counter runs of this benchmark (FETCH_SIZE, then WRITE_SIZE;
-    both in KiB per dispatch) into HBM bytes per launch of the partition
+    both in KiB per dispatch) into HBM bytes per launch of the dominant
     kernel, each scaled by what the same counter reads for the plain device
     copy of known size in the same run, and store them with the hash of the
     kernel source they describe."""
+    kname = traffic_kernel(shared)
     out = {}
     for name, d in (("fetch", fetch_dir), ("write", write_dir)):
         rows = _counter_rows(d)
-        part = [v for k, v in rows if "decode_partition_kernel" in k]
+        part = [v for k, v in rows if kname in k]
         copy = [v for k, v in rows if "copyBuffer" in k or "copy" in k.lower()]
         copy = max(copy)  # the probe copy is the largest copy dispatch
         scale = (copy_bytes / 1024.0) / copy
@@ -113,12 +122,13 @@ def record_traffic(workload, fetch_dir, write_dir, copy_bytes):
                      "dispatches": len(part)}
     fetch = out["fetch"]["partition_kernel_kib_avg"] * 1024 * out["fetch"]["scale"]
     write = out["write"]["partition_kernel_kib_avg"] * 1024 * out["write"]["scale"]
-    rec = {"kernel": "decode_partition_kernel", "workload": f"{workload} (bench.py --workload {workload})",
-           "kernel_source_sha256": kernel_source_hash(), "hbm_bytes_per_launch": round(fetch + write),
+    flags = f"--workload {workload}" + (" --plain" if workload == "prefix13b" and not shared else "")
+    rec = {"kernel": kname, "workload": f"{workload} (bench.py {flags})",
+           "kernel_source_sha256": kernel_source_hash(shared), "hbm_bytes_per_launch": round(fetch + write),
            "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write), "counters": out}
     import paged_kv_cache_391_amd as pa
     rec["partition_tokens"] = pa.decode_partition_tokens()
-    with open(traffic_file(workload), "w") as f:
+    with open(traffic_file(workload, shared), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec, indent=1))
 
@@ -262,8 +272,8 @@ def main():
                     help="store HBM bytes per launch from two rocprofv3 --pmc runs of this script and exit")
     args = ap.parse_args()
     if args.record_traffic:
-        record_traffic(args.workload, args.record_traffic[0], args.record_traffic[1],
-                       int(args.copy_probe_gib * (1 << 30)))
+        record_traffic(args.workload, args.workload == "prefix13b" and not args.plain, args.record_traffic[0],
+                       args.record_traffic[1], int(args.copy_probe_gib * (1 << 30)))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         log("bench.py measures one GPU only: each GPU would run this path on its own share of sequences or "
@@ -479,10 +489,10 @@ def main():
     del src, dst
 
     traffic = None
-    tf = traffic_file(args.workload)
+    tf = traffic_file(args.workload, shared)
     if os.path.exists(tf):
         rec = json.load(open(tf))
-        if rec.get("kernel_source_sha256") == kernel_source_hash() and rec.get("partition_tokens") == P:
+        if rec.get("kernel_source_sha256") == kernel_source_hash(shared) and rec.get("partition_tokens") == P:
             traffic = rec.get("hbm_bytes_per_launch")
 
     cpu = None
@@ -512,7 +522,7 @@ def main():
                    "partition_tokens": P, "parallelism": "none (1 GPU)"},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(k2_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(k2_gbps / HBM_PEAK_GBPS, 4), "traffic": None if shared else traffic,
+                     "frac": round(k2_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": ("shared-prefix decode call (shared, tail and reduction kernels)" if shared
                                 else f"decode_partition_kernel<{wl.dtype},{D},{bs}>"),
                      "bytes_per_launch": k2_bytes, "avg_launch_us": round(k2_cold_ms * 1e3, 2),
@@ -539,7 +549,10 @@ def main():
         rec["aliasing"] = {"path": "shared-prefix decode" if shared else "plain decode",
                            "logical_kv_bytes": logical_kv, "unique_kv_bytes": kv,
                            "logical_GBps": round(logical_kv / (k2_cold_ms * 1e-3) / 1e9, 1),
-                           "unique_GBps": round(kv / (k2_cold_ms * 1e-3) / 1e9, 1)}
+                           "unique_GBps": round(kv / (k2_cold_ms * 1e-3) / 1e9, 1),
+                           # counter-measured HBM bytes of the dominant kernel (the partition kernel, or
+                           # the shared-prefix step kernel) over the same time, when recorded for this build
+                           "hbm_GBps": None if traffic is None else round(traffic / (k2_cold_ms * 1e-3) / 1e9, 1)}
     if p is not None:
         pf_tflops = pf_flops / (pf_ms * 1e-3) / 1e12
         rec["phases_us"]["prefill"] = round(pf_ms * 1e3, 2)
