@@ -1,0 +1,78 @@
+"""bench.py's contract: one GPU only, the algorithmic byte counts behind its
+rates, and the JSON line it prints."""
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=60)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
+    assert r.stdout.strip() == ""
+
+
+def test_decode_bytes_by_hand():
+    # two sequences of 1 and 17 tokens, 2 heads x 4 dims, 2-byte elements, blocks of 16
+    kv, table, qo = bench.decode_bytes(np.array([1, 17]), 2, 4, 2, 16)
+    assert kv == (1 + 17) * 2 * 4 * 2 * 2          # K and V of every valid token
+    assert table == (1 + 2) * 4 + 2 * 4             # one entry per used block, one length per sequence
+    assert qo == 2 * 2 * 2 * 4 * 2                  # q and out rows
+
+
+def test_partition_kernel_bytes_by_hand():
+    # 600 tokens split into two 512-token partitions: (m, l, acc) per partition in fp32;
+    # 100 tokens in one partition: the output row in the input type
+    ctx = np.array([600, 100])
+    kv, table, _ = bench.decode_bytes(ctx, 2, 4, 2, 16)
+    q = 2 * 2 * 4 * 2
+    writes = 2 * 2 * (4 + 2) * 4 + 2 * 4 * 2
+    assert bench.partition_kernel_bytes(ctx, 2, 4, 2, 16, 512) == kv + table + q + writes
+
+
+def test_unique_kv_bytes_counts_aliased_slots_once():
+    bt = np.array([[3, 5], [3, 6]], dtype=np.int32)  # both rows alias block 3
+    ctx = np.array([20, 18])
+    got = bench.unique_kv_bytes(bt, ctx, 2, 4, 2, 16)
+    slots = 16 + 4 + 2  # block 3 once, 4 tokens of block 5, 2 of block 6
+    assert got == slots * 2 * 4 * 2 * 2
+
+
+def test_prefill_work_by_hand():
+    class P:
+        query_start_loc = np.array([0, 3])
+        context_lens = np.array([5])
+    flops, byts = bench.prefill_work(P, 1, 4, 2)
+    # 3 queries after 2 cached tokens: 2*3 + (1+2+3) = 12 unmasked pairs, 4 flops per pair per dim
+    assert flops == 4 * 4 * 1 * (3 * 2 + 6)
+    assert byts == 5 * 1 * 4 * 2 * 2 + 2 * 3 * 1 * 4 * 2
+
+
+@pytest.mark.gpu
+def test_bench_prints_one_json_line_with_the_contract():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "3", "--warmup", "1",
+                        "--no-cpu-baseline", "--copy-probe-gib", "0.25"], capture_output=True, text=True,
+                       timeout=240, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stdout.splitlines() if ln.strip()]
+    assert len(lines) == 1
+    rec = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "scaling",
+                "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"):
+        assert key in rec
+    assert rec["n_gpus"] == 1 and rec["steps"] == 3 and rec["warmup"] == 1
+    assert rec["unit"] == "GB/s" and rec["higher_is_better"] is True and rec["data"] == "synthetic"
+    assert "workload" in rec["config"]
+    rf = rec["roofline"]
+    assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
+    assert 0.2 < rf["frac"] < 1.0 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
+    assert 0 < rec["value"] < 8000.0
