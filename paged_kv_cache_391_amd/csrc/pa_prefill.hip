@@ -49,44 +49,73 @@ namespace {
 #ifndef PA_PREFILL_NQ
 #define PA_PREFILL_NQ 2
 #endif
-#ifndef PA_PREFILL_R
-#define PA_PREFILL_R 2
-#endif
 constexpr int KT = PA_PREFILL_KT;  // keys per tile (32 or 64)
 constexpr int NQ = PA_PREFILL_NQ;  // 16-query groups per wave
 constexpr int QW = 16 * NQ;        // queries per wave
 constexpr int QT = 4 * QW;         // queries per workgroup
-constexpr int R = PA_PREFILL_R;    // register sets: tile t+R is fetched while tile t is computed
-constexpr int UNR = R % 2 == 0 ? R : 2 * R;  // loop unroll: a multiple of R and of the two LDS buffers
+constexpr int NBUF = 3;            // LDS buffers per operand: tile t computed while t+1, t+2 land
 constexpr float RESCALE_LOG2 = 8.f; // lazy rescale threshold (log2 units): p < 256 between rescales
-static_assert(KT == 32 || KT == 64, "key tile must be 32 or 64");
+static_assert(KT == 32, "key tile of 32");
+
+// 16 bytes per lane from global memory straight into LDS: lane L's bytes
+// land at LDS byte offset lds_off + 16 L (lds_off wave-uniform, via M0).
+// Written as inline assembly so that the compiler, which waits for every
+// such load before any later LDS read, leaves the waits to the kernel; the
+// loads count in vmcnt like any vector load.
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds_off)
+               : "memory", "m0");
+}
+// wait until at most N of this wave's vector loads are outstanding
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N == 0 || N == 2 || N == 4, "supported counts");
+  if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+// block ids through the scalar cache, as inline assembly: once the DMA
+// assembly is in the kernel the compiler can no longer prove the table
+// unchanged and would read it with vector loads, whose waits would drain
+// the DMA queue. (Waits on lgkmcnt only: LDS and scalar loads.)
+__device__ __forceinline__ int32_t sload1(const int32_t* p) {
+  int32_t v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ void sload2(const int32_t* p0, const int32_t* p1, int32_t& v0, int32_t& v1) {
+  asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
+               : "=s"(v0), "=s"(v1) : "s"(p0), "s"(p1) : "memory");
+}
+template <typename T> __device__ __forceinline__ uint32_t lds_offset(T* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)p;
+}
 
 }  // namespace
 
 template <Dt DT, int D, int BS>
-__global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void prefill_mfma_kernel(const PrefillArgs a) {
   constexpr int KS = D / 32;     // MFMA k-steps over head_dim for Q.K
   constexpr int NDT = D / 16;    // 16-row tiles of O^T
   constexpr int NSUB = KT / 16;  // 16-key subtiles of S^T
   constexpr int NKST = KT / 32;  // MFMA k-steps over keys for P.V
   constexpr int CPR = D / 8;     // 16-byte chunks per K/V row
   constexpr int ROWB = D * 2;    // bytes per K/V row
-  constexpr int KROW = D + 8;    // K tile row stride in LDS (halves), padded against bank conflicts
-  constexpr int VROW = KT + 4;   // V^T tile row stride in LDS (halves)
-  constexpr int NKC = KT * CPR;          // K chunks per tile
-  constexpr int NVP = (KT / 2) * CPR;    // V (key pair, chunk) items per tile
-  constexpr int KCH = NKC / 256;
-  constexpr int VPR = (NVP + 255) / 256;
-  // one load of a wave covers KW consecutive keys of K, VW of V (in pairs)
-  constexpr int KW = 64 / CPR;
-  constexpr int VW = 2 * 64 / CPR;
-  constexpr bool V_ONE_BLOCK = VW <= BS;
-  static_assert(NKC % 256 == 0, "whole K chunks per thread");
-  static_assert(KW <= BS && BS % KW == 0, "a wave's K rows of one load lie in one block");
-  static_assert(V_ONE_BLOCK || VW == 2 * BS, "a wave's V rows of one load span at most two blocks");
+  constexpr int TILEB = KT * ROWB;       // bytes of one K (or V) tile in LDS
+  constexpr int PR = 1024 / ROWB;        // rows per 1 KiB DMA piece (one wave-wide load)
+  constexpr int PPW = TILEB / 1024 / 4;  // pieces per wave, per operand and tile
+  constexpr int DMAS = 2 * PPW;          // DMA loads per wave and tile (K and V)
+  static_assert(PR <= BS && BS % PR == 0, "the rows of one DMA piece lie in one block");
+  static_assert(PPW >= 1, "every wave loads a piece of each tile");
 
-  __shared__ __align__(16) uint16_t sk[2][KT * KROW];
-  __shared__ __align__(16) uint16_t sv[2][D * VROW];
+  // K and V tiles row-major in LDS, unpadded; 16-byte chunk c of row r sits
+  // at chunk position c ^ f(r), which spreads the MFMA operand reads over
+  // all banks: K is read 16 rows at one chunk (f = r mod 16, or (r/2) mod 8
+  // for 8-chunk rows), V^T by transposing reads of 4 rows x 2 chunks per
+  // 16 lanes (f = 2r mod 16, or r & 6).
+  __shared__ __align__(1024) uint8_t sk[NBUF][TILEB];
+  __shared__ __align__(1024) uint8_t sv[NBUF][TILEB];
+  auto fk = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+  auto fv = [](int r) { return D == 128 ? ((2 * r) & 15) : (r & 6); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -151,87 +180,50 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
   constexpr uint32_t ONE2 = ones2<DT>();
   const u32x4 ones = u32x4{ONE2, ONE2, ONE2, ONE2};
 
-  // wave-uniform address of row `key` (tile-absolute) of head h, its block
-  // id read through the scalar cache; keys past the sequence's blocks read
-  // the last block's rows (zeroed when staged)
-  auto row_base = [&](const char* cache, int key) -> const char* {
-    const uint32_t k = (uint32_t)key;
-    const uint32_t blk = min(k / BS, (uint32_t)(nb - 1));
-    const uint32_t phys = (uint32_t)bt_row[blk];
-    return cache + ((uint64_t)phys * blk_bytes + (head_bytes + (k % BS) * ROWB));
-  };
-  // per-lane byte offsets inside a wave's rows of one load
-  const uint32_t k_lane = lane * 16;
-  uint32_t v_lane[2];
+  // DMA of one tile into LDS buffer b: piece p holds rows p*PR .. p*PR+PR-1
+  // and wave w loads pieces w, w+4, ...; lane L of a piece fills chunk
+  // position L % CPR of row L / CPR, i.e. source chunk (L % CPR) ^ f(row).
+  // The swizzle terms repeat every 16 rows, so the per-lane source offsets
+  // are the same for every piece and tile.
+  const int prow = lane / CPR;
+  const int pcol = lane % CPR;
+  const uint32_t k_src = prow * ROWB + ((pcol ^ fk(wave * PR + prow)) * 16);
+  const uint32_t v_src = prow * ROWB + ((pcol ^ fv(wave * PR + prow)) * 16);
+  const uint32_t sk0 = lds_offset(&sk[0][0]);
+  const uint32_t sv0 = lds_offset(&sv[0][0]);
+  auto dma = [&](int t, int b) {
+    int key[PPW], phys[PPW];  // each piece's first row (wave-uniform) and its block
 #pragma unroll
-  for (int e = 0; e < 2; ++e)
-    v_lane[e] = ((2 * (lane / CPR) + e) % (V_ONE_BLOCK ? VW : BS)) * ROWB + (lane % CPR) * 16;
-
-  // ---- global -> registers for one tile. Every load is issued
-  // unconditionally, so all of a tile's loads are in flight together.
-  u32x4 kreg[R][KCH], vreg[R][2 * VPR];
-  auto fetch = [&](u32x4 (&kr)[KCH], u32x4 (&vr)[2 * VPR], int t) {
-    const int kv0 = t * KT;
+    for (int i = 0; i < PPW; ++i) key[i] = t * KT + (wave + 4 * i) * PR;
+    auto entry = [&](int k) { return bt_row + min((uint32_t)k / BS, (uint32_t)(nb - 1)); };
+    if constexpr (PPW == 2) sload2(entry(key[0]), entry(key[1]), phys[0], phys[1]);
+    else phys[0] = sload1(entry(key[0]));
 #pragma unroll
-    for (int r = 0; r < KCH; ++r) {
-      const int key = kv0 + (wave * 64 + 256 * r) / CPR;
-      kr[r] = *reinterpret_cast<const u32x4*>(row_base(kc, key) + k_lane);
-    }
-#pragma unroll
-    for (int r = 0; r < VPR; ++r) {
-      const int pw = min(wave * 64 + 256 * r, NVP - 64);  // waves past the tile's pairs repeat the last ones
-      const int key = kv0 + 2 * (pw / CPR);
-      if constexpr (V_ONE_BLOCK) {
-        const char* base = row_base(vc, key);
-#pragma unroll
-        for (int e = 0; e < 2; ++e) vr[2 * r + e] = *reinterpret_cast<const u32x4*>(base + v_lane[e]);
-      } else {  // lanes 0..31 read the first block, 32..63 the next
-        const char* b0 = row_base(vc, key);
-        const char* b1 = row_base(vc, key + BS);
-        const char* base = lane < 32 ? b0 : b1;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) vr[2 * r + e] = *reinterpret_cast<const u32x4*>(base + v_lane[e]);
-      }
+    for (int i = 0; i < PPW; ++i) {
+      const int p = wave + 4 * i;
+      const uint64_t row = (uint64_t)(uint32_t)phys[i] * blk_bytes + (head_bytes + ((uint32_t)key[i] % BS) * ROWB);
+      lds_dma16(kc + row + k_src, sk0 + b * TILEB + p * 1024);
+      lds_dma16(vc + row + v_src, sv0 + b * TILEB + p * 1024);
     }
   };
-  // ---- registers -> LDS buffer b: K row-major, V transposed (two keys
-  // packed per word); rows at or past kv_end (last tile only) become zeros
-  auto stage = [&](int b, int t, const u32x4 (&kr)[KCH], const u32x4 (&vr)[2 * VPR]) {
-    const int kv0 = t * KT;
-    auto put = [&](bool tail) {
-      const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int r = 0; r < KCH; ++r) {
-        const int key = (wave * 64 + 256 * r) / CPR + lane / CPR;
-        const int dc = lane % CPR;
-        *reinterpret_cast<u32x4*>(&sk[b][key * KROW + dc * 8]) = (tail && kv0 + key >= kv_end) ? z : kr[r];
-      }
-#pragma unroll
-      for (int r = 0; r < VPR; ++r) {
-        const int pw = wave * 64 + 256 * r;
-        if (NVP % 256 == 0 || pw < NVP) {
-          const int kp = pw / CPR + lane / CPR;
-          const int dc = lane % CPR;
-          const u32x4 v0 = (tail && kv0 + 2 * kp >= kv_end) ? z : vr[2 * r];
-          const u32x4 v1 = (tail && kv0 + 2 * kp + 1 >= kv_end) ? z : vr[2 * r + 1];
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            // element 2w of keys 2kp, 2kp+1 (low halves), then element 2w+1 (high halves)
-            const uint32_t lo = __builtin_amdgcn_perm(v1[w], v0[w], 0x05040100u);
-            const uint32_t hi = __builtin_amdgcn_perm(v1[w], v0[w], 0x07060302u);
-            *reinterpret_cast<uint32_t*>(&sv[b][(dc * 8 + 2 * w) * VROW + 2 * kp]) = lo;
-            *reinterpret_cast<uint32_t*>(&sv[b][(dc * 8 + 2 * w + 1) * VROW + 2 * kp]) = hi;
-          }
-        }
-      }
-    };
-    if (kv0 + KT > kv_end) put(true);
-    else put(false);
+  // rows at or past kv_end of the last tile: V rows become zeros (their
+  // weights are zero, but the slots may hold anything, NaN included)
+  auto zero_tail = [&](int t, int b) {
+    const int r0 = kv_end - t * KT;
+    for (int i = tid; i < (KT - r0) * CPR; i += 256)
+      *reinterpret_cast<u32x4*>(&sv[b][(r0 + i / CPR) * ROWB + (i % CPR) * 16]) = u32x4{0u, 0u, 0u, 0u};
   };
+  // MFMA operand offsets (bytes inside a buffer): K fragment of k-step ks is
+  // chunk 4 ks + g4 of row n16 (+16 rows per subtile); V^T fragment rows
+  // come from keys 4 g4 + n16/4 (+16), dims 16 dt + 4 (n16 % 4).
+  uint32_t k_rd[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) k_rd[ks] = n16 * ROWB + (((4 * ks + g4) ^ fk(n16)) * 16);
+  const int vkey = 4 * g4 + (n16 >> 2);
+  // chunk 2 dt + (n16 % 4) / 2 of row vkey sits at (2 dt + a) ^ fv = 2 (dt ^ fv/2) + a: the dt term
+  // enters by an XOR of dt << 5 into bits that are zero in the rest of the offset
+  const uint32_t v_rd = vkey * ROWB + (((n16 & 3) >> 1) * 16) + 8 * (n16 & 1) + ((fv(vkey) >> 1) << 5);
 
-  // |scale| * log2(e), floored at the smallest normal float so that a
-  // masked score (-inf) times c stays -inf: a zero scale then weighs every
-  // allowed key equally to within 1e-26
   const float c = fmaxf(a.scale_log2, 1.17549435e-38f);
   auto compute = [&](int b, int kv0) {
     // S^T = K Q^T over NSUB key subtiles of 16
@@ -244,7 +236,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
     for (int sub = 0; sub < NSUB; ++sub) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 ka = *reinterpret_cast<const u32x4*>(&sk[b][(sub * 16 + n16) * KROW + ks * 32 + 8 * g4]);
+        const u32x4 ka = *reinterpret_cast<const u32x4*>(&sk[b][sub * 16 * ROWB + k_rd[ks]]);
 #pragma unroll
         for (int g = 0; g < NQ; ++g) sacc[g][sub] = mfma16<DT>(ka, qf[g][ks], sacc[g][sub]);
       }
@@ -311,20 +303,24 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
         }
       }
     }
-    // O^T += V^T P^T: A = V^T rows d = 16*dt + n16, keys 32*kst + 4*g4 + {0..3} and +16
+    // O^T += V^T P^T: A = V^T rows d = 16*dt + n16, keys 4*g4 + {0..3} and 16 + 4*g4 + {0..3}, two
+    // transposing 8-byte LDS reads (each 16 lanes turn 4 key rows x 16 dims around)
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const uint8_t* vb = &sv[b][0];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
+      const uint32_t off = v_rd ^ (dt << 5);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) void*)(vb + off));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) void*)(vb + off + 16 * ROWB));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+      const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+      const u32x4 va = u32x4{l2[0], l2[1], h2[0], h2[1]};
 #pragma unroll
-      for (int kst = 0; kst < NKST; ++kst) {
-        const uint16_t* row = &sv[b][(dt * 16 + n16) * VROW + kst * 32 + 4 * g4];
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(row);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 16);
-        const u32x4 va = u32x4{lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-        for (int g = 0; g < NQ; ++g) {
-          o[g][dt] = mfma16<DT>(va, pb[g][kst], o[g][dt]);
-          if constexpr (DT == Dt::BF16) o[g][dt] = mfma16<DT>(va, pbl[g][kst], o[g][dt]);
-        }
+      for (int g = 0; g < NQ; ++g) {
+        o[g][dt] = mfma16<DT>(va, pb[g][0], o[g][dt]);
+        if constexpr (DT == Dt::BF16) o[g][dt] = mfma16<DT>(va, pbl[g][0], o[g][dt]);
       }
     }
 #pragma unroll
@@ -336,27 +332,33 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
       }
   };
 
-  // R register sets in a ring and two LDS buffers: while tile t is
-  // computed, tile t+R travels global -> registers (set t % R) and tile t+1,
-  // fetched R-1 tiles earlier, is staged into the other LDS buffer; one
-  // barrier per tile. Fetches and stages are unconditional (past the end
-  // they re-read the last tile, an L2 hit, and stage zeros that are never
-  // read) so the compiler can prove each set's loads were consumed before it
-  // is refilled and never drains the load queue early.
+  // Pipeline over tiles with three LDS buffers: tile t+2's DMA is issued
+  // while tile t is computed (tile t+1's is in flight). Each iteration waits
+  // until this wave's loads of tile t have landed (the DMA loads of t+1 may
+  // stay outstanding), then a barrier makes every wave's share visible and
+  // guarantees that all waves are done with tile t-1, whose buffer the DMA
+  // of t+2 reuses. DMAs past the last tile re-read it (never used).
+  // The Q loads must be complete before the first DMA: otherwise the wait
+  // the compiler places at their first use, inside the loop, would drain
+  // the DMA queue on every iteration.
 #pragma unroll
-  for (int r = 0; r < R; ++r) fetch(kreg[r], vreg[r], min(r, n_tiles - 1));
-  stage(0, 0, kreg[0], vreg[0]);
-  __syncthreads();
-  for (int t0 = 0; t0 < n_tiles; t0 += UNR) {
+  for (int g = 0; g < NQ; ++g)
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int t = t0 + u;
-      fetch(kreg[u % R], vreg[u % R], min(t + R, n_tiles - 1));
-      if (wave_active && t < n_tiles && t * KT <= wave_last_pos) compute(u & 1, t * KT);
-      stage((u + 1) & 1, t + 1, kreg[(u + 1) % R], vreg[(u + 1) % R]);
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qf[g][ks]));
+  dma(0, 0);
+  dma(min(1, n_tiles - 1), 1);
+  for (int t = 0; t < n_tiles; ++t) {
+    const int b = t % NBUF;
+    wait_vmcnt<DMAS>();
+    __syncthreads();
+    if ((t + 1) * KT > kv_end) {
+      zero_tail(t, b);
       __syncthreads();
     }
+    dma(min(t + 2, n_tiles - 1), (t + 2) % NBUF);
+    if (wave_active && t * KT <= wave_last_pos) compute(b, t * KT);
   }
+  wait_vmcnt<0>();  // no DMA may still be writing this workgroup's LDS when it ends
 
   if (!wave_active) return;
   // finish: every row of lacc holds the query's denominator
