@@ -11,18 +11,20 @@
 // Orientation: the wave computes S^T = K Q^T (keys on the MFMA rows, its
 // queries on the columns) and O^T += V^T P^T. In that orientation the
 // score accumulator a lane holds (one query, four keys per 16-key subtile)
-// is exactly the B operand P^T needs, so P never leaves registers; the
-// price is a transposed V tile, which the workgroup writes into LDS while
-// staging it. Per tile of KT keys:
-//   * addressing is scalar: every global load of a wave covers a few
-//     consecutive keys that lie in one block, so the wave reads the block's
-//     id with a scalar load (the scalar cache keeps the table row), forms
-//     the row address in scalar registers and adds only a fixed per-lane
-//     offset;
-//   * 256 threads gather each K tile (row-major) and V tile (transposed,
-//     key pairs packed with v_perm) into one of two LDS buffers; tile t+R's
-//     global loads are in flight while tile t is computed and tile t+1 is
-//     staged, one barrier per tile; only the last tile clamps and zeroes;
+// is exactly the B operand P^T needs, so P never leaves registers; the V^T
+// operand comes from LDS through transposing reads. Per tile of KT keys:
+//   * the tile's K and V rows travel from global memory straight into LDS
+//     (global_load_lds_dwordx4: each wave moves 1 KiB pieces, lane L's 16
+//     bytes landing at the piece base + 16 L), three buffers deep, so tile
+//     t+2 is in flight while tile t is computed; one barrier per tile. The
+//     rows of a piece lie in one block, so each piece's block id is read
+//     with a scalar load and the source address is that block's row plus a
+//     fixed per-lane offset;
+//   * tiles are row-major with the 16-byte chunks XOR-swizzled per row, so
+//     the K fragment reads and the V^T reads (ds_read_b64_tr_b16, which
+//     turns 4 key rows x 16 dims around per 16 lanes) use every bank once;
+//   * only the last tile is clamped (its rows past the context read the
+//     last block) and has its V rows past the context zeroed in LDS;
 //   * each wave owns NQ groups of 16 queries; every K or V^T fragment read
 //     from LDS feeds one MFMA per group;
 //   * online softmax per query: the max over the raw scores (the scale is
