@@ -9,9 +9,13 @@
 
 // Decode tuning: heads per workgroup (one wave each), the number of waves
 // per SIMD the partition kernel's register budget must leave room for, and
-// tokens per split-K partition.
+// tokens per split-K partition. One head per workgroup: consecutive
+// workgroups take consecutive heads of a row, so the rows of one head are H
+// workgroups apart; workgroups go round-robin over the chip's 8 XCDs, and
+// with H a multiple of 8 all rows of a head run on one XCD, where sequences
+// that alias the same blocks share its L2.
 #ifndef PA_DECODE_HEADS
-#define PA_DECODE_HEADS 2
+#define PA_DECODE_HEADS 1
 #endif
 #ifndef PA_DECODE_MIN_WAVES
 #define PA_DECODE_MIN_WAVES 5
