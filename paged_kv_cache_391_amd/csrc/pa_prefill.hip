@@ -18,8 +18,10 @@
 //     bytes landing at the piece base + 16 L), three buffers deep, so tile
 //     t+2 is in flight while tile t is computed; one barrier per tile. The
 //     rows of a piece lie in one block, so each piece's block id is read
-//     with a scalar load and the source address is that block's row plus a
-//     fixed per-lane offset;
+//     with a scalar load (issued before the barrier, whose wait hides its
+//     latency) and the source address is that block's row, in SGPRs, plus
+//     a fixed per-lane offset; the tile loop is unrolled three times, so
+//     every LDS offset is an immediate;
 //   * tiles are row-major with the 16-byte chunks XOR-swizzled per row, so
 //     the K fragment reads and the V^T reads (ds_read_b64_tr_b16, which
 //     turns 4 key rows x 16 dims around per 16 lanes) use every bank once;
@@ -29,7 +31,8 @@
 //     from LDS feeds one MFMA per group;
 //   * online softmax per query: the max over the raw scores (the scale is
 //     applied once to it, and inside the exponent's FMA), cross-row max on
-//     the row-swap instructions, P narrowed with the packed converts; the
+//     the row-swap instructions (both query groups folded together), P
+//     narrowed with the packed converts; the
 //     denominator is summed on the matrix cores (a block of ones in V^T);
 //     only tiles that cross a wave's first query carry the causal mask (the
 //     masked scores are set to -inf), tiles past its last query are skipped, and
@@ -40,6 +43,8 @@
 // negative scale is applied as |scale| on negated queries (exact: a sign
 // flip), so the max of the raw scores is the max of the scaled ones.
 #include "pa_internal.h"
+
+#include <type_traits>
 
 namespace pa {
 
@@ -60,33 +65,63 @@ constexpr float RESCALE_LOG2 = 8.f; // lazy rescale threshold (log2 units): p < 
 static_assert(KT == 32, "key tile of 32");
 
 // 16 bytes per lane from global memory straight into LDS: lane L's bytes
-// land at LDS byte offset lds_off + 16 L (lds_off wave-uniform, via M0).
+// land at LDS byte offset lds_off + 16 L (lds_off wave-uniform, via M0);
+// the source is a wave-uniform 64-bit base in SGPRs plus a 32-bit per-lane
+// byte offset, so the address adds happen in the load, not in VALU.
 // Written as inline assembly so that the compiler, which waits for every
 // such load before any later LDS read, leaves the waits to the kernel; the
 // loads count in vmcnt like any vector load.
-__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_off) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds_off)
+__device__ __forceinline__ void lds_dma16s(const char* sbase, uint32_t voff, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_off)
                : "memory", "m0");
 }
-// wait until at most N of this wave's vector loads are outstanding
-template <int N> __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N == 0 || N == 2 || N == 4, "supported counts");
-  if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+// max without the NaN-quieting the compiler adds around values of unknown
+// origin (the scores are never signalling NaNs); the wait states let a
+// following v_permlane read the result
+__device__ __forceinline__ float vmax_nc(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2\n\ts_nop 1" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
-// block ids through the scalar cache, as inline assembly: once the DMA
+// Row maxima of two values at once: afterwards every lane holds the max of
+// a over the four lanes n16, n16+16, n16+32, n16+48, and the same for b.
+// The first swap pairs a's odd rows with b's even rows, so one max folds
+// both values' row pairs into one register; the row-pair swap folds the
+// halves; the last swap hands a's result to every row of one register and
+// b's to the other.
+__device__ __forceinline__ void rows4_max2(float& a, float& b) {
+  const auto s1 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, a), __builtin_bit_cast(int, b), false, false);
+  const float x = vmax_nc(__builtin_bit_cast(float, (int)s1[0]), __builtin_bit_cast(float, (int)s1[1]));
+  const auto s2 = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x), false, false);
+  const float y = vmax_nc(__builtin_bit_cast(float, (int)s2[0]), __builtin_bit_cast(float, (int)s2[1]));
+  const auto s3 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, y), __builtin_bit_cast(int, y), false, false);
+  a = __builtin_bit_cast(float, (int)s3[0]);
+  b = __builtin_bit_cast(float, (int)s3[1]);
+}
+// wait until none of this wave's vector loads is outstanding
+__device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Block ids through the scalar cache, as inline assembly: once the DMA
 // assembly is in the kernel the compiler can no longer prove the table
 // unchanged and would read it with vector loads, whose waits would drain
 // the DMA queue. (Waits on lgkmcnt only: LDS and scalar loads.)
-__device__ __forceinline__ int32_t sload1(const int32_t* p) {
-  int32_t v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
-  return v;
-}
 __device__ __forceinline__ void sload2(const int32_t* p0, const int32_t* p1, int32_t& v0, int32_t& v1) {
   asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
-               : "=s"(v0), "=s"(v1) : "s"(p0), "s"(p1) : "memory");
+               : "=&s"(v0), "=&s"(v1) : "s"(p0), "s"(p1) : "memory");
+}
+// The top of a pipeline step: the scalar loads of the next DMA's block ids
+// (PPW of them), the wait until at most 2 PPW of this wave's DMA loads are
+// outstanding, the workgroup barrier, then the wait for the scalar loads,
+// whose latency thus hides behind the barrier.
+template <int PPW>
+__device__ __forceinline__ void sload_barrier(const int32_t* const (&e)[PPW], int32_t (&v)[PPW]) {
+  static_assert(PPW == 1 || PPW == 2, "one or two DMA pieces per wave");
+  if constexpr (PPW == 2)
+    asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt vmcnt(4)\n\ts_barrier\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&s"(v[0]), "=&s"(v[1]) : "s"(e[0]), "s"(e[1]) : "memory");
+  else
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt vmcnt(2)\n\ts_barrier\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&s"(v[0]) : "s"(e[0]) : "memory");
 }
 template <typename T> __device__ __forceinline__ uint32_t lds_offset(T* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)p;
@@ -105,7 +140,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   constexpr int TILEB = KT * ROWB;       // bytes of one K (or V) tile in LDS
   constexpr int PR = 1024 / ROWB;        // rows per 1 KiB DMA piece (one wave-wide load)
   constexpr int PPW = TILEB / 1024 / 4;  // pieces per wave, per operand and tile
-  constexpr int DMAS = 2 * PPW;          // DMA loads per wave and tile (K and V)
   static_assert(PR <= BS && BS % PR == 0, "the rows of one DMA piece lie in one block");
   static_assert(PPW >= 1, "every wave loads a piece of each tile");
 
@@ -193,19 +227,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   const uint32_t v_src = prow * ROWB + ((pcol ^ fv(wave * PR + prow)) * 16);
   const uint32_t sk0 = lds_offset(&sk[0][0]);
   const uint32_t sv0 = lds_offset(&sv[0][0]);
-  auto dma = [&](int t, int b) {
-    int key[PPW], phys[PPW];  // each piece's first row (wave-uniform) and its block
-#pragma unroll
-    for (int i = 0; i < PPW; ++i) key[i] = t * KT + (wave + 4 * i) * PR;
-    auto entry = [&](int k) { return bt_row + min((uint32_t)k / BS, (uint32_t)(nb - 1)); };
-    if constexpr (PPW == 2) sload2(entry(key[0]), entry(key[1]), phys[0], phys[1]);
-    else phys[0] = sload1(entry(key[0]));
+  // block-table entry of piece i of tile t (clamped to the blocks read)
+  auto entry = [&](int t, int i) {
+    const uint32_t k = (uint32_t)(t * KT + (wave + 4 * i) * PR);
+    return bt_row + min(k / BS, (uint32_t)(nb - 1));
+  };
+  // DMA of tile t into buffer b given its pieces' block ids
+  auto dma_ids = [&](int t, int b, const int (&phys)[PPW]) {
 #pragma unroll
     for (int i = 0; i < PPW; ++i) {
       const int p = wave + 4 * i;
-      const uint64_t row = (uint64_t)(uint32_t)phys[i] * blk_bytes + (head_bytes + ((uint32_t)key[i] % BS) * ROWB);
-      lds_dma16(kc + row + k_src, sk0 + b * TILEB + p * 1024);
-      lds_dma16(vc + row + v_src, sv0 + b * TILEB + p * 1024);
+      const uint32_t key = (uint32_t)(t * KT + p * PR);
+      const uint64_t row = (uint64_t)(uint32_t)phys[i] * blk_bytes + (head_bytes + (key % BS) * ROWB);
+      lds_dma16s(kc + row, k_src, sk0 + b * TILEB + p * 1024);
+      lds_dma16s(vc + row, v_src, sv0 + b * TILEB + p * 1024);
     }
   };
   // rows at or past kv_end of the last tile: V rows become zeros (their
@@ -227,7 +262,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   const uint32_t v_rd = vkey * ROWB + (((n16 & 3) >> 1) * 16) + 8 * (n16 & 1) + ((fv(vkey) >> 1) << 5);
 
   const float c = fmaxf(a.scale_log2, 1.17549435e-38f);
-  auto compute = [&](int b, int kv0) {
+  auto compute = [&](auto bc, int kv0) {
+    constexpr int b = decltype(bc)::value;
     // S^T = K Q^T over NSUB key subtiles of 16
     f32x4 sacc[NQ][NSUB];
 #pragma unroll
@@ -264,14 +300,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
     }
     u32x4 pb[NQ][NKST];
     u32x4 pbl[NQ][NKST];  // bf16 remainders
+    static_assert(NQ == 2, "row maxima of the two query groups are taken together");
+    float mrow[NQ];  // max of the raw scores (c > 0: the scaled max is mr * c)
 #pragma unroll
     for (int g = 0; g < NQ; ++g) {
-      float mr = -INFINITY;  // max of the raw scores (c > 0: the scaled max is mr * c)
+      float mr = -INFINITY;
 #pragma unroll
       for (int sub = 0; sub < NSUB; ++sub)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mr = fmaxf(mr, sacc[g][sub][i]);
-      const float mt = rows4_max(mr) * c;
+      mrow[g] = mr;
+    }
+    rows4_max2(mrow[0], mrow[1]);
+#pragma unroll
+    for (int g = 0; g < NQ; ++g) {
+      const float mt = mrow[g] * c;
       const bool grow = mt > m[g] + RESCALE_LOG2;  // also true for the first tile (m = -inf)
       if (__any(grow)) {
         const float m_new = grow ? mt : m[g];
@@ -347,20 +390,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   for (int g = 0; g < NQ; ++g)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qf[g][ks]));
-  dma(0, 0);
-  dma(min(1, n_tiles - 1), 1);
-  for (int t = 0; t < n_tiles; ++t) {
-    const int b = t % NBUF;
-    wait_vmcnt<DMAS>();
-    __syncthreads();
+  const int last = n_tiles - 1;
+  {
+    int p0[PPW], p1[PPW];
+    if constexpr (PPW == 2) {
+      sload2(entry(0, 0), entry(0, 1), p0[0], p0[1]);
+      sload2(entry(min(1, last), 0), entry(min(1, last), 1), p1[0], p1[1]);
+    } else {
+      sload2(entry(0, 0), entry(min(1, last), 0), p0[0], p1[0]);
+    }
+    dma_ids(0, 0, p0);
+    dma_ids(min(1, last), 1, p1);
+  }
+  // one iteration, buffer b = t mod 3 known at compile time (the loop is
+  // unrolled three times), so LDS offsets are immediates
+  auto iter = [&](int t, auto bc) {
+    constexpr int b = decltype(bc)::value;
+    const int tn = min(t + 2, last);
+    const int32_t* e[PPW];
+    int ids[PPW];
+#pragma unroll
+    for (int i = 0; i < PPW; ++i) e[i] = entry(tn, i);
+    sload_barrier<PPW>(e, ids);
     if ((t + 1) * KT > kv_end) {
       zero_tail(t, b);
       __syncthreads();
     }
-    dma(min(t + 2, n_tiles - 1), (t + 2) % NBUF);
-    if (wave_active && t * KT <= wave_last_pos) compute(b, t * KT);
+    dma_ids(tn, (b + 2) % NBUF, ids);
+    if (wave_active && t * KT <= wave_last_pos) compute(bc, t * KT);
+  };
+  for (int t = 0; t < n_tiles; t += 3) {
+    iter(t, std::integral_constant<int, 0>{});
+    if (t + 1 < n_tiles) iter(t + 1, std::integral_constant<int, 1>{});
+    if (t + 2 < n_tiles) iter(t + 2, std::integral_constant<int, 2>{});
   }
-  wait_vmcnt<0>();  // no DMA may still be writing this workgroup's LDS when it ends
+  wait_vmcnt0();  // no DMA may still be writing this workgroup's LDS when it ends
 
   if (!wave_active) return;
   // finish: every row of lacc holds the query's denominator

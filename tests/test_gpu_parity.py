@@ -252,6 +252,96 @@ def test_decode_bit_identical_with_aliased_or_private_prefix_blocks():
     assert np.abs(base.astype(np.float64) - ref).max() <= ATOL["f16"]
 
 
+def _to_big_pool(kc, vc, nb_big):
+    """Copy a compact pool's blocks into a pool of nb_big blocks: even block
+    ids stay, odd ones move to the top of the pool (byte offsets past
+    2^32). Returns the big caches and the old id -> new id map."""
+    nb = kc.shape[0]
+    ids = torch.arange(nb, device="cuda")
+    new_id = torch.where(ids % 2 == 0, ids, nb_big - 1 - ids)
+    kb = torch.empty((nb_big,) + tuple(kc.shape[1:]), dtype=kc.dtype, device="cuda")
+    vb = torch.empty_like(kb)
+    kb[new_id] = kc
+    vb[new_id] = vc
+    return kb, vb, new_id
+
+
+def _same_bits(a, b):
+    """Bitwise equality (the pools hold NaN poison in never-written slots)."""
+    iv = {2: torch.int16, 4: torch.int32}[a.element_size()]
+    return a.shape == b.shape and torch.equal(a.contiguous().view(iv), b.contiguous().view(iv))
+
+
+def _remap_tables(bt, new_id):
+    out = bt.clone()
+    valid = bt >= 0
+    out[valid] = new_id[bt[valid].long()].int()
+    return out
+
+
+def test_pool_beyond_4gib_is_bit_identical():
+    """Caches of more than 4 GiB each, with half of the workload's blocks at
+    ids whose byte offsets pass 2^32: the cache write, block copies, the
+    gather, the decode, the shared-prefix decode and the prefill give bit for
+    bit what they give on the compact pool (every offset is 64-bit)."""
+    wl = config4(prompts=4, samples=4, prompt_len=256, max_tail=64, cow=True)
+    H, D, bs = wl.num_heads, wl.head_dim, wl.block_size
+    block_bytes = H * bs * D * 2
+    nb_big = (9 << 29) // block_bytes + 2 * wl.num_blocks  # > 4.5 GiB per cache
+    assert (nb_big - 2 * wl.num_blocks) * block_bytes > (1 << 32)
+    od = OnDevice(wl)
+    kb, vb, new_id = _to_big_pool(od.k_cache, od.v_cache, nb_big)
+    # cache write through remapped slots
+    slots = od.slot_mapping.long()
+    big_slots = torch.where(slots >= 0, new_id[(slots // bs).clamp(min=0)] * bs + slots % bs, slots).int()
+    od.write_new_tokens()
+    pa.reshape_and_cache(od.new_k, od.new_v, kb, vb, big_slots)
+    assert _same_bits(kb[new_id], od.k_cache) and _same_bits(vb[new_id], od.v_cache)
+    d = wl.decode
+    bt_big = _remap_tables(od.block_tables, new_id)
+    # decode, plain and shared-prefix
+    base = od.decode(torch.float32)
+    got = od.decode(torch.float32, block_tables=bt_big, k_cache=kb, v_cache=vb)
+    assert _same_bits(base, got)
+    gs, pl, samples = _groups_for_prefix_workload(wl)
+    ws = pa.make_decode_shared_workspace(d.num_seqs, H, D, d.max_context_len)
+    sh = [torch.empty(od.q.shape, dtype=torch.float32, device="cuda") for _ in range(2)]
+    for o, (bt, k, v) in zip(sh, [(od.block_tables, od.k_cache, od.v_cache), (bt_big, kb, vb)]):
+        pa.paged_attention_decode_shared_prefix(o, od.q, k, v, bt, od.context_lens, dev(gs), dev(pl), wl.scale,
+                                                d.max_context_len, samples, int(pl.max()), ws)
+    assert _same_bits(sh[0], sh[1])
+    # gather
+    cu = dev(np.concatenate([[0], np.cumsum(d.context_lens)]).astype(np.int32))
+    total = int(d.context_lens.sum())
+    outs = []
+    for bt, k, v in [(od.block_tables, od.k_cache, od.v_cache), (bt_big, kb, vb)]:
+        ko = torch.empty((total, H, D), dtype=k.dtype, device="cuda")
+        vo = torch.empty_like(ko)
+        pa.gather_kv(ko, vo, k, v, bt, od.context_lens, cu, d.max_context_len)
+        outs.append((ko, vo))
+    assert _same_bits(outs[0][0], outs[1][0]) and _same_bits(outs[0][1], outs[1][1])
+    # block copies between the two halves of the id range
+    pairs = np.array([[1, 2], [4, 3], [5, 7]], dtype=np.int32)
+    pa.copy_blocks(od.k_cache, od.v_cache, dev(pairs))
+    pa.copy_blocks(kb, vb, new_id[torch.from_numpy(pairs).long().cuda()].int().contiguous())
+    assert _same_bits(kb[new_id], od.k_cache) and _same_bits(vb[new_id], od.v_cache)
+    del kb, vb
+    # prefill of a chunk workload with the same cache shape, in a big pool
+    pw = prefill_workload("pf_big", 790, "f16", H, D, bs, [0, 200, 37], [100, 64, 130], maxb=20, pool_factor=1.2)
+    op = _on_device_written(pw)
+    kp, vp, pid = _to_big_pool(op.k_cache, op.v_cache, nb_big)
+    p = pw.prefill
+    res = []
+    for bt, k, v in [(op.pf_block_tables, op.k_cache, op.v_cache), (_remap_tables(op.pf_block_tables, pid), kp, vp)]:
+        o = torch.empty(op.pf_q.shape, dtype=torch.float32, device="cuda")
+        pa.paged_attention_prefill(o, op.pf_q, k, v, bt, op.pf_context_lens, op.pf_qsl, pw.scale,
+                                   max_q_len=p.max_q_len, max_context_len=p.max_context_len)
+        res.append(o)
+    assert _same_bits(res[0], res[1])
+    del kp, vp
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------- shared-prefix decode
 
 def _groups_for_prefix_workload(wl):
@@ -388,6 +478,27 @@ def test_prefill_head_dim_64(dtype, bs):
     p = wl.prefill
     ref = oracle.prefill(p.q, kc, vc, p.block_tables, p.context_lens, p.query_start_loc, wl.scale, dtype)
     got = host(od.prefill(torch.float32)).astype(np.float64)
+    err = np.abs(got - ref).max()
+    assert err <= ATOL[dtype], f"prefill max abs err {err:.3e}"
+
+
+@pytest.mark.parametrize("dtype,bs", [("f16", 8), ("bf16", 16), ("f16", 32), ("bf16", 64)])
+def test_prefill_tile_aligned_contexts(dtype, bs):
+    """Contexts and chunk starts on multiples of the 32-key tile: the last key
+    tile is full (no rows past the context to clear), and query tiles start
+    exactly on key-tile edges. The pool's unused slots hold NaN poison, so a
+    read past a context shows up as a non-finite output."""
+    prior = [0, 32, 64, 96, 224]
+    chunk = [32, 32, 64, 160, 64]
+    maxb = math.ceil(max(p + c for p, c in zip(prior, chunk)) / bs)
+    wl = prefill_workload(f"pf_aligned_{dtype}_{bs}", 780 + bs, dtype, 3, 128, bs, prior, chunk, maxb=maxb,
+                          pool_factor=1.2)
+    od = _on_device_written(wl)
+    kc, vc = oracle.reshape_and_cache(wl.new.k, wl.new.v, wl.k_cache, wl.v_cache, wl.new.slot_mapping, bs, dtype)
+    p = wl.prefill
+    ref = oracle.prefill(p.q, kc, vc, p.block_tables, p.context_lens, p.query_start_loc, wl.scale, dtype)
+    got = host(od.prefill(torch.float32)).astype(np.float64)
+    assert np.isfinite(got).all()
     err = np.abs(got - ref).max()
     assert err <= ATOL[dtype], f"prefill max abs err {err:.3e}"
 
