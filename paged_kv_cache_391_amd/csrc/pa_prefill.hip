@@ -70,7 +70,10 @@ static_assert(KT == 32, "key tile of 32");
 // byte offset, so the address adds happen in the load, not in VALU.
 // Written as inline assembly so that the compiler, which waits for every
 // such load before any later LDS read, leaves the waits to the kernel; the
-// loads count in vmcnt like any vector load.
+// loads count in vmcnt like any vector load. M0 is written in the same
+// assembly block as the load that reads it (one wait state between them),
+// and the compiled kernel uses M0 nowhere else, so clobbering a register
+// the compiler does not preserve around inline assembly loses nothing.
 __device__ __forceinline__ void lds_dma16s(const char* sbase, uint32_t voff, uint32_t lds_off) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_off)
                : "memory", "m0");

@@ -1,8 +1,13 @@
 // The library driven through its C ABI alone (no Python, no torch): device
 // buffers from hipMalloc, the new tokens written with pa_reshape_and_cache,
-// a split-K pa_paged_attention_decode, the fp32 output copied back and
-// compared with the fp64 oracle (linked from oracle/liboracle.so; test code
-// only). Prints "max_abs_err <x>" and exits 0 when x <= 2e-3.
+// a split-K pa_paged_attention_decode and a causal pa_paged_attention_prefill
+// whose fp32 outputs are copied back and compared with the fp64 oracle
+// (linked from oracle/liboracle.so; test code only), then the same three
+// parts as one pa_attention_step (the pa_step_args struct filled from C), in
+// order and with the prefill on a side stream, each equal bit for bit to
+// the separate calls. Prints "max_abs_err <x>", "prefill_max_abs_err <y>"
+// and "step_bit_identical <0|1>"; exits 0 when x, y <= 2e-3 and the step
+// results are identical.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -20,6 +25,10 @@ extern "C" int oracle_decode(double* out, const void* q, const void* k_cache, co
                              const int32_t* bt, const int32_t* ctx, int S, int H, int d, int bs, int num_blocks,
                              int max_blocks, double scale, int dtype, const int32_t* pairs, int npairs,
                              int nthreads);
+extern "C" int oracle_prefill(double* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* bt, const int32_t* ctx, const int32_t* qsl, int S, int H, int d,
+                              int bs, int num_blocks, int max_blocks, double scale, int dtype, const int32_t* rows,
+                              int nrows, int nthreads);
 
 #define HIP_OK(x)                                                              \
   do {                                                                         \
@@ -150,5 +159,107 @@ int main() {
   double err = 0.0;
   for (size_t i = 0; i < out.size(); ++i) err = std::fmax(err, std::fabs((double)out[i] - ref[i]));
   std::printf("max_abs_err %.3e\n", err);
-  return err <= 2e-3 ? 0 : 1;
+
+  // ---- causal prefill: the last 40 tokens of sequence 1 and the last 100 of
+  // sequence 2 as query chunks over the same cache
+  const int PS = 2, TQ = 140;
+  const int32_t qsl[PS + 1] = {0, 40, 140};
+  const int32_t pctx[PS] = {ctx[1], ctx[2]};
+  std::vector<int32_t> pbt(bt.begin() + max_blocks, bt.end());
+  std::vector<uint16_t> pq((size_t)TQ * H * D);
+  for (auto& x : pq) x = next_half(st);
+  void *dpq, *dpout;
+  int32_t *dpbt, *dpctx, *dqsl;
+  HIP_OK(hipMalloc(&dpq, pq.size() * 2));
+  HIP_OK(hipMalloc(&dpout, (size_t)TQ * H * D * 4));
+  HIP_OK(hipMalloc(&dpbt, pbt.size() * 4));
+  HIP_OK(hipMalloc(&dpctx, PS * 4));
+  HIP_OK(hipMalloc(&dqsl, (PS + 1) * 4));
+  HIP_OK(hipMemcpy(dpq, pq.data(), pq.size() * 2, hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(dpbt, pbt.data(), pbt.size() * 4, hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(dpctx, pctx, PS * 4, hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(dqsl, qsl, (PS + 1) * 4, hipMemcpyHostToDevice));
+  PA_OK_(pa_paged_attention_prefill(dpout, PA_F32, dpq, dkc, dvc, dpbt, dpctx, dqsl, PS, TQ, 100, H, H, D, BS, NB,
+                                    max_blocks, 700, scale, PA_F16, stream));
+  std::vector<float> pout((size_t)TQ * H * D);
+  HIP_OK(hipStreamSynchronize(stream));
+  HIP_OK(hipMemcpy(pout.data(), dpout, pout.size() * 4, hipMemcpyDeviceToHost));
+  std::vector<int32_t> rows;
+  for (int r = 0; r < TQ; ++r)
+    for (int h = 0; h < H; ++h) rows.insert(rows.end(), {r, h});
+  std::vector<double> pref((size_t)TQ * H * D);
+  if (oracle_prefill(pref.data(), pq.data(), kc.data(), vc.data(), pbt.data(), pctx, qsl, PS, H, D, BS, NB,
+                     max_blocks, scale, 1, rows.data(), TQ * H, 1) != 0) {
+    std::printf("oracle prefill failed\n");
+    return 5;
+  }
+  double perr = 0.0;
+  for (size_t i = 0; i < pout.size(); ++i) perr = std::fmax(perr, std::fabs((double)pout[i] - pref[i]));
+  std::printf("prefill_max_abs_err %.3e\n", perr);
+
+  // ---- the same work as one scheduler step: the cache write (the same rows
+  // into the same slots again), the prefill and the decode
+  void *dsdec, *dspf;
+  HIP_OK(hipMalloc(&dsdec, (size_t)S * H * D * 4));
+  HIP_OK(hipMalloc(&dspf, (size_t)TQ * H * D * 4));
+  pa_step_args a;
+  std::memset(&a, 0, sizeof(a));
+  a.k_cache = dkc;
+  a.v_cache = dvc;
+  a.num_blocks = NB;
+  a.num_heads = H;
+  a.head_dim = D;
+  a.block_size = BS;
+  a.dtype = PA_F16;
+  a.scale = scale;
+  a.new_k = dnk;
+  a.new_v = dnv;
+  a.slot_mapping = dslots;
+  a.num_new_tokens = S;
+  a.prefill_out = dspf;
+  a.prefill_out_dtype = PA_F32;
+  a.prefill_q = dpq;
+  a.prefill_block_tables = dpbt;
+  a.prefill_context_lens = dpctx;
+  a.prefill_query_start_loc = dqsl;
+  a.num_prefill_seqs = PS;
+  a.prefill_total_q = TQ;
+  a.prefill_max_q_len = 100;
+  a.prefill_max_blocks_per_seq = max_blocks;
+  a.prefill_max_context_len = 700;
+  a.decode_out = dsdec;
+  a.decode_out_dtype = PA_F32;
+  a.decode_q = dq;
+  a.decode_block_tables = dbt;
+  a.decode_context_lens = dctx;
+  a.num_decode_seqs = S;
+  a.decode_max_blocks_per_seq = max_blocks;
+  a.decode_max_context_len = 700;
+  a.workspace = dws;
+  a.workspace_bytes = ws_bytes;
+  hipStream_t side;
+  hipEvent_t fork, join;
+  HIP_OK(hipStreamCreate(&side));
+  HIP_OK(hipEventCreateWithFlags(&fork, hipEventDisableTiming));
+  HIP_OK(hipEventCreateWithFlags(&join, hipEventDisableTiming));
+  int identical = 1;
+  for (int mode = 0; mode < 2; ++mode) {
+    HIP_OK(hipMemsetAsync(dsdec, 0xff, (size_t)S * H * D * 4, stream));
+    HIP_OK(hipMemsetAsync(dspf, 0xff, (size_t)TQ * H * D * 4, stream));
+    PA_OK_(pa_attention_step(&a, stream, mode ? side : nullptr, mode ? fork : nullptr, mode ? join : nullptr));
+    HIP_OK(hipStreamSynchronize(stream));
+    std::vector<float> sdec(out.size()), spf(pout.size());
+    HIP_OK(hipMemcpy(sdec.data(), dsdec, sdec.size() * 4, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(spf.data(), dspf, spf.size() * 4, hipMemcpyDeviceToHost));
+    if (std::memcmp(sdec.data(), out.data(), out.size() * 4) != 0 ||
+        std::memcmp(spf.data(), pout.data(), pout.size() * 4) != 0)
+      identical = 0;
+  }
+  // a side stream equal to the main stream is refused before anything runs
+  if (pa_attention_step(&a, stream, stream, fork, join) != PA_ERR_INVALID_ARG) {
+    std::printf("side stream == stream was not refused\n");
+    return 4;
+  }
+  std::printf("step_bit_identical %d\n", identical);
+  return (err <= 2e-3 && perr <= 2e-3 && identical) ? 0 : 1;
 }

@@ -1,7 +1,9 @@
 """The library driven from C++ through include/pagedattn.h alone (no Python
 binding, no torch): tests/c_abi/decode_from_c.cpp writes new tokens with
-pa_reshape_and_cache, runs a split-K pa_paged_attention_decode and compares
-the fp32 output with the fp64 oracle."""
+pa_reshape_and_cache, runs a split-K pa_paged_attention_decode and a causal
+pa_paged_attention_prefill and compares their fp32 outputs with the fp64
+oracle, then runs the same work as one pa_attention_step (in order and with
+a side stream) and checks it equals the separate calls bit for bit."""
 import os
 import subprocess
 
@@ -16,10 +18,12 @@ def test_c_program_compiles_against_the_header():
 
 
 @pytest.mark.gpu
-def test_c_program_decode_matches_the_oracle():
+def test_c_program_matches_the_oracle_and_the_step_call():
     if not os.path.exists(c_abi_build.EXE):
         c_abi_build.build()
     r = subprocess.run([c_abi_build.EXE], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
-    err = float(r.stdout.split("max_abs_err")[1].split()[0])
-    assert err <= 2e-3
+    vals = dict(line.split() for line in r.stdout.split("\n") if line.strip())
+    assert float(vals["max_abs_err"]) <= 2e-3
+    assert float(vals["prefill_max_abs_err"]) <= 2e-3
+    assert vals["step_bit_identical"] == "1"
