@@ -38,8 +38,16 @@
 
 namespace pa {
 
+// Occupancy target: f16/bf16 (and f32 at head dim 64) fit the two tile
+// buffers in the VGPRs of PA_DECODE_MIN_WAVES waves per SIMD; f32 rows of
+// 128 dims carry twice the bytes per lane and need ~162 VGPRs, so those
+// kernels ask for three waves per SIMD instead of spilling to scratch.
+template <Dt DT, int D> constexpr int decode_min_waves() {
+  return DT == Dt::F32 && D == 128 ? 3 : PA_DECODE_MIN_WAVES;
+}
+
 template <Dt DT, int D, int BS, int HG, RowMode MODE>
-__global__ __launch_bounds__(HG * 64, PA_DECODE_MIN_WAVES) void decode_partition_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(HG * 64, (decode_min_waves<DT, D>())) void decode_partition_kernel(const DecodeArgs a) {
   decode_partition_body<DT, D, BS, HG, MODE>(a, blockIdx.x, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
 }
 

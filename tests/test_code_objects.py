@@ -1,0 +1,77 @@
+"""The built library's gfx950 code objects: no kernel spills registers to
+scratch memory, and the hot kernels keep the register budgets their
+occupancy relies on. Reads the AMDGPU metadata notes of this repository's
+own build (the .hip_fatbin section of libpagedattn.so) with the LLVM tools
+that ship with ROCm; needs no GPU."""
+import os
+import re
+import shutil
+import struct
+import subprocess
+
+import pytest
+
+import paged_kv_cache_391_amd as pa
+
+LLVM = "/opt/rocm/llvm/bin"
+MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
+
+pytestmark = pytest.mark.skipif(
+    not os.path.exists(pa.LIB_PATH) or not os.path.exists(os.path.join(LLVM, "llvm-readelf")),
+    reason="library not built or LLVM tools missing")
+
+
+def _kernels(tmp_path):
+    """{kernel symbol: {metadata key: value}} over every gfx950 code object
+    in the library's offload bundles."""
+    fatbin = tmp_path / "fatbin.bin"
+    subprocess.run([os.path.join(LLVM, "llvm-objcopy"), f"--dump-section=.hip_fatbin={fatbin}", pa.LIB_PATH,
+                    str(tmp_path / "stripped.so")], check=True)
+    data = fatbin.read_bytes()
+    kernels = {}
+    for i, start in enumerate(m.start() for m in re.finditer(re.escape(MAGIC), data)):
+        p = start + len(MAGIC)
+        (entries,) = struct.unpack_from("<Q", data, p)
+        p += 8
+        for _ in range(entries):
+            off, size, tlen = struct.unpack_from("<QQQ", data, p)
+            p += 24
+            triple = data[p:p + tlen].decode()
+            p += tlen
+            if "gfx950" not in triple:
+                continue
+            co = tmp_path / f"co{i}.o"
+            co.write_bytes(data[start + off:start + off + size])
+            notes = subprocess.run([os.path.join(LLVM, "llvm-readelf"), "--notes", str(co)], check=True,
+                                   capture_output=True, text=True).stdout
+            # one metadata map per kernel: split at each "- .agpr_count" list item
+            for block in re.split(r"\n\s+- \.agpr_count:", notes)[1:]:
+                name = re.search(r"\.name:\s+(\S+)", block).group(1)
+                kernels[name] = {k: int(v) for k, v in re.findall(
+                    r"\.(vgpr_count|vgpr_spill_count|sgpr_spill_count|private_segment_fixed_size|"
+                    r"group_segment_fixed_size):\s+(\d+)", block)}
+    return kernels
+
+
+def test_no_kernel_uses_scratch(tmp_path):
+    ks = _kernels(tmp_path)
+    assert len(ks) > 100, "expected every instantiation of every kernel"
+    bad = {n: m for n, m in ks.items()
+           if m["vgpr_spill_count"] or m["sgpr_spill_count"] or m["private_segment_fixed_size"]}
+    assert not bad, f"kernels spilling to scratch: {sorted(bad)[:5]}"
+
+
+def test_hot_kernels_keep_their_occupancy(tmp_path):
+    """512 VGPRs per SIMD lane: five waves per SIMD for the f16/bf16 decode
+    partitions (<= 96 VGPRs, granularity 8), three for the prefill and the
+    f32 decode at head dim 128 (<= 168)."""
+    ks = _kernels(tmp_path)
+    dec16 = [m for n, m in ks.items() if "decode_partition_kernel" in n and re.search(r"DtE[12]E", n)]
+    dec32 = [m for n, m in ks.items() if "decode_partition_kernel" in n and "DtE0ELi128" in n]
+    pf = [m for n, m in ks.items() if "prefill_mfma_kernel" in n]
+    assert dec16 and dec32 and pf
+    assert max(m["vgpr_count"] for m in dec16) <= 96
+    assert max(m["vgpr_count"] for m in dec32) <= 168
+    assert max(m["vgpr_count"] for m in pf) <= 168
+    # the prefill's three LDS buffers per operand (48 KiB) let three workgroups share a CU's 160 KiB
+    assert max(m["group_segment_fixed_size"] for m in pf) <= 160 * 1024 // 3
