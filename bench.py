@@ -17,6 +17,10 @@ Other workloads (``--workload``), same machinery:
   mixed_step  40 x 128, f16, block_size 16: cache write of 2048 rows, causal
               prefill of 4 chunks (L ~ U[256,512] after U[0,1024] cached
               tokens) and decode of 96 sequences (ctx ~ U[256,4096])
+  prefill_long  40 x 128, f16, block_size 16: cache write of the chunks'
+              4096 rows, then causal prefill of 8 chunks of 512 queries after
+              1536 cached tokens (150 GFLOP): the compute-bound path, reported
+              in TFLOP/s against the dense MFMA peak
 
 One step = the workload's whole path, all inputs resident in HBM:
 reshape_and_cache of the step's new tokens, [prefill,] then split-K decode
@@ -63,7 +67,10 @@ WORKLOADS = {
     "mixed_step": "mixed_step: reshape_and_cache of 2048 rows + causal prefill of 4 chunks (L U[256,512], prior "
                   "U[0,1024]) + split-K decode of 96 seqs (ctx U[256,4096]), 40 heads x 128, f16, block_size 16, "
                   "seed 396",
+    "prefill_long": "prefill_long: reshape_and_cache of the chunks' 4096 rows + causal prefill of 8 chunks of 512 "
+                    "queries after 1536 cached tokens, 40 heads x 128, f16, block_size 16, seed 397",
 }
+PREFILL_METRIC = "causal paged prefill achieved TFLOP/s (% of the dense MFMA peak)"
 
 
 def traffic_file(workload, shared=False):
@@ -252,6 +259,187 @@ def cpu_baseline(wl, threads, alg_bytes, sample_bytes):
             "host": {"cpu_model": model, "usable_cores": avail}}
 
 
+def prefill_config():
+    from workloads import prefill_workload
+    return prefill_workload("prefill_long", 397, "f16", 40, 128, 16, [1536] * 8, [512] * 8, maxb=128)
+
+
+def _oracle_prefill_rate(wl, kc, vc, pairs, threads, seconds):
+    """TFLOP/s of the oracle's causal prefill over the given (query row,
+    head) pairs (4 d flops per visible key), repeated until `seconds`."""
+    import numpy as np
+    import oracle
+    p = wl.prefill
+    L = np.diff(p.query_start_loc)
+    seq = np.searchsorted(p.query_start_loc, pairs[:, 0], side="right") - 1
+    visible = p.context_lens[seq] - L[seq] + (pairs[:, 0] - p.query_start_loc[seq]) + 1
+    flops = float(4 * wl.head_dim * visible.astype(np.int64).sum())
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.prefill(p.q, kc, vc, p.block_tables, p.context_lens, p.query_start_loc, wl.scale, wl.dtype,
+                       rows=pairs, threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 1000:
+            break
+    return flops * reps / el / 1e12, reps, el
+
+
+def prefill_main(args):
+    """The compute-bound path: one step = the chunks' cache write + the
+    causal prefill; value = prefill flops per step time (TFLOP/s); roofline =
+    the prefill kernel, cold, against the dense f16 MFMA peak."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import paged_kv_cache_391_amd as pa
+    from tests._gpu import OnDevice
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    t = time.time()
+    wl = prefill_config()
+    p = wl.prefill
+    log(f"[bench] {args.workload}: generated in {time.time() - t:.1f}s: {wl.num_blocks} blocks, {p.total_q} queries")
+    od = OnDevice(wl)
+    H, D, elt = wl.num_heads, wl.head_dim, wl.elt_bytes
+    out = torch.empty_like(od.pf_q)  # output in the input dtype
+    flops, pf_bytes = prefill_work(p, H, D, elt)
+    T = int(wl.new.slot_mapping.shape[0])
+    cache_write_bytes = 4 * T * H * D * elt + 4 * T
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        pa.reshape_and_cache(od.new_k, od.new_v, od.k_cache, od.v_cache, od.slot_mapping)
+        if ev is not None:
+            ev[1].record()
+        pa.paged_attention_prefill(out, od.pf_q, od.k_cache, od.v_cache, od.pf_block_tables, od.pf_context_lens,
+                                   od.pf_qsl, wl.scale, max_q_len=p.max_q_len, max_context_len=p.max_context_len)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    cw_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    pf_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    eager_out = out.clone()
+
+    # cold pass: a 1 GiB read before every step evicts L2 and the MALL
+    scratch = torch.zeros((args.evict_mib << 20) // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros((), dtype=torch.float32, device="cuda")
+    cold = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        if args.evict_mode == "read":
+            torch.sum(scratch, dim=0, out=sink)
+        else:
+            scratch.fill_(float(i))
+        step(cold[i])
+    torch.cuda.synchronize()
+    del scratch, sink
+    cold_pf = np.array([e[1].elapsed_time(e[2]) for e in cold])
+    if not torch.equal(out, eager_out):
+        raise SystemExit("cold-cache step output differs from the warm one")
+
+    ms_per_step, graph_ok = eager_ms, None
+    if not args.eager:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph_ok = True
+        for _ in range(max(1, args.warmup)):
+            out.zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+            graph_ok = graph_ok and bool(torch.equal(out, eager_out))
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        if not graph_ok:
+            raise SystemExit("graph replay disagrees with the eager step")
+
+    peak = MFMA_PEAK_TFLOPS[wl.dtype]
+    cold_ms = float(cold_pf.mean())
+    pf_tflops = flops / (cold_ms * 1e-3) / 1e12
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    log(f"[bench] {ms_per_step * 1e3:.1f} us/step ({'graph' if not args.eager else 'eager'}; eager "
+        f"{eager_ms * 1e3:.1f} us): cache write {cw_ms * 1e3:.1f} us, prefill {pf_ms * 1e3:.1f} us warm "
+        f"({flops / (pf_ms * 1e-3) / 1e12:.0f} TFLOP/s), {cold_ms * 1e3:.1f} us cold ({pf_tflops:.0f} TFLOP/s), "
+        f"graph output == eager: {graph_ok}")
+
+    def pct(x):
+        return {"mean": round(float(x.mean()) * 1e3, 2), "median": round(float(np.median(x)) * 1e3, 2),
+                "p10": round(float(np.percentile(x, 10)) * 1e3, 2), "p90": round(float(np.percentile(x, 90)) * 1e3, 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        kc, vc = oracle.reshape_and_cache(wl.new.k, wl.new.v, wl.k_cache, wl.v_cache, wl.new.slot_mapping,
+                                          wl.block_size, wl.dtype)
+        threads = max(1, min(16, _host_cpu()[1]))
+        last = int(p.query_start_loc[-2])
+        many = np.stack(np.meshgrid(np.arange(last, last + 128), np.arange(H), indexing="ij"), -1).reshape(-1, 2)
+        few = many[:256]
+        rate, reps, el = _oracle_prefill_rate(wl, kc, vc, many.astype(np.int32), threads, CPU_SECONDS)
+        rate1, reps1, el1 = _oracle_prefill_rate(wl, kc, vc, few.astype(np.int32), 1, CPU_SECONDS)
+        model, avail = _host_cpu()
+        cpu = {"value": round(rate, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+               "sample": f"fp64 causal prefill of the first 128 queries of the last chunk x {H} heads "
+                         f"({many.shape[0]} (query, head) rows), {reps} pass(es) in {el:.1f} s; 4 d flops per "
+                         "visible key, the definition of value",
+               "one_thread": {"value": round(rate1, 6), "unit": "TFLOP/s", "cores": 1,
+                              "sample": f"the first {few.shape[0]} of those rows, {reps1} pass(es) in {el1:.1f} s"},
+               "host": {"cpu_model": model, "usable_cores": avail}}
+
+    rec = {
+        "metric": PREFILL_METRIC,
+        "value": round(value, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.workload], "global_batch": int(p.num_seqs),
+                   "seq_len": int(p.max_context_len), "parallelism": "none (1 GPU)"},
+        "pct_of_peak": round(100 * value / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(pf_tflops, 1), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(pf_tflops / peak, 4), "traffic": None,
+                     "kernel": f"prefill_mfma_kernel<{wl.dtype},{D},{wl.block_size}>",
+                     "flops_per_launch": flops, "bytes_per_launch": pf_bytes,
+                     "avg_launch_us": round(cold_ms * 1e3, 2),
+                     "timing": f"HIP events on the launch stream around each of {args.steps} eager launches, "
+                               f"each after a {args.evict_mib} MiB {args.evict_mode} that evicts L2 and MALL",
+                     "launch_us": pct(cold_pf), "warm_avg_launch_us": round(pf_ms * 1e3, 2),
+                     "hbm_frac": round(pf_bytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "roofline_us": round(max(flops / (peak * 1e12), pf_bytes / (HBM_PEAK_GBPS * 1e9)) * 1e6, 2)},
+        "timing": "hip_graph_replay" if not args.eager else "eager",
+        "eager_ms_per_step": round(eager_ms, 5),
+        "step_bytes": cache_write_bytes + pf_bytes,
+        "phases_us": {"reshape_and_cache": round(cw_ms * 1e3, 2), "prefill": round(pf_ms * 1e3, 2)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -272,6 +460,8 @@ def main():
                     help="store HBM bytes per launch from two rocprofv3 --pmc runs of this script and exit")
     args = ap.parse_args()
     if args.record_traffic:
+        if args.workload == "prefill_long":
+            raise SystemExit("traffic records cover the decode kernels only")
         record_traffic(args.workload, args.workload == "prefix13b" and not args.plain, args.record_traffic[0],
                        args.record_traffic[1], int(args.copy_probe_gib * (1 << 30)))
         return
@@ -279,6 +469,12 @@ def main():
         log("bench.py measures one GPU only: each GPU would run this path on its own share of sequences or "
             "heads with no collective in the timed region, so only --gpus 1 is measured.")
         sys.exit(2)
+
+    if args.workload == "prefill_long":
+        if args.block_size is not None or args.plain:
+            raise SystemExit("--block-size and --plain do not apply to prefill_long")
+        prefill_main(args)
+        return
 
     import numpy as np
     import torch

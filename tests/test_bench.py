@@ -76,3 +76,30 @@ def test_bench_prints_one_json_line_with_the_contract():
     assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
     assert 0.2 < rf["frac"] < 1.0 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
     assert 0 < rec["value"] < 8000.0
+
+
+def test_prefill_long_workload_and_its_flops():
+    """8 chunks of 512 queries after 1536 cached tokens, 40 heads x 128:
+    4 d H (L c + L(L+1)/2) per chunk = 150.37 GFLOP per step."""
+    wl = bench.prefill_config()
+    p = wl.prefill
+    assert p.num_seqs == 8 and p.total_q == 8 * 512
+    assert (np.asarray(p.context_lens) == 2048).all()
+    flops, byts = bench.prefill_work(p, wl.num_heads, wl.head_dim, wl.elt_bytes)
+    assert flops == 8 * 4 * 128 * 40 * (512 * 1536 + 512 * 513 // 2) == 150_365_798_400
+    assert byts == 8 * (2048 * 40 * 128 * 2 * 2 + 2 * 512 * 40 * 128 * 2)
+
+
+@pytest.mark.gpu
+def test_bench_prefill_long_prints_the_mfma_roofline():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "prefill_long", "--steps", "3",
+                        "--warmup", "1", "--no-cpu-baseline"], capture_output=True, text=True, timeout=240,
+                       cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stdout.splitlines() if ln.strip()]
+    assert len(lines) == 1
+    rec = json.loads(lines[0])
+    assert rec["unit"] == "TFLOP/s" and rec["n_gpus"] == 1
+    rf = rec["roofline"]
+    assert rf["bound"] == "mfma" and rf["unit"] == "TFLOP/s" and rf["peak"] == 2500.0
+    assert 0.05 < rf["frac"] < 1.0 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
