@@ -426,7 +426,9 @@ def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens
                             max_q_len: int | None = None, max_context_len: int | None = None):
     """Causal attention of query chunks: chunk ``s`` is rows
     ``query_start_loc[s]:query_start_loc[s+1]`` and the last L_s tokens of
-    its ``context_lens[s]``-token context."""
+    its ``context_lens[s]``-token context. ``max_q_len`` and
+    ``max_context_len`` left as None are read from the device tensors, which
+    waits for the stream; pass them to keep the call asynchronous."""
     _dev(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc)
     _i32(block_tables, context_lens, query_start_loc)
     nb, H, bs, D = _cache_dims(k_cache, v_cache)
@@ -439,9 +441,9 @@ def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens
     if query_start_loc.shape != (S + 1,):
         raise ValueError("query_start_loc must be [num_seqs + 1]")
     if max_q_len is None:
-        max_q_len = int((query_start_loc[1:] - query_start_loc[:-1]).max().item()) if S else 0
+        max_q_len = int((query_start_loc[1:] - query_start_loc[:-1]).max().item()) if S else 0  # synchronises
     if max_context_len is None:
-        max_context_len = int(context_lens.max().item()) if S else 0
+        max_context_len = int(context_lens.max().item()) if S else 0  # synchronises
     _check("paged_attention_prefill", lib().pa_paged_attention_prefill(
         _ptr(out), _DT[out.dtype], _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         _ptr(query_start_loc), S, TQ, int(max_q_len), H, H, D, bs, nb, int(block_tables.shape[1]),
