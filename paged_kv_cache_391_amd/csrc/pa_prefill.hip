@@ -314,19 +314,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
         for (int i = 0; i < 4; ++i) mr = fmaxf(mr, sacc[g][sub][i]);
       mrow[g] = mr;
     }
-    rows4_max2(mrow[0], mrow[1]);
+    // A row's max exceeds its reference by more than 2^RESCALE_LOG2 exactly
+    // when one of its four lanes' maxima does (the row's lanes share m, and
+    // x -> x * c is monotonic), so a lane-local test decides; the cross-row
+    // max runs only on the tiles that raise some row (the first one, m =
+    // -inf, and the rare jumps), and those take the same decisions as before.
+    bool jump = false;
+#pragma unroll
+    for (int g = 0; g < NQ; ++g) jump |= mrow[g] * c > m[g] + RESCALE_LOG2;
+    if (__any(jump)) {
+      rows4_max2(mrow[0], mrow[1]);
+#pragma unroll
+      for (int g = 0; g < NQ; ++g) {
+        const float mt = mrow[g] * c;
+        const bool grow = mt > m[g] + RESCALE_LOG2;
+        if (__any(grow)) {
+          const float m_new = grow ? mt : m[g];
+          const float alpha = __builtin_amdgcn_exp2f(m[g] - m_new);
+          lacc[g] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) o[g][dt] *= alpha;
+          m[g] = m_new;
+        }
+      }
+    }
 #pragma unroll
     for (int g = 0; g < NQ; ++g) {
-      const float mt = mrow[g] * c;
-      const bool grow = mt > m[g] + RESCALE_LOG2;  // also true for the first tile (m = -inf)
-      if (__any(grow)) {
-        const float m_new = grow ? mt : m[g];
-        const float alpha = __builtin_amdgcn_exp2f(m[g] - m_new);
-        lacc[g] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[g][dt] *= alpha;
-        m[g] = m_new;
-      }
       const float neg_m = m[g] == -INFINITY ? 0.f : -m[g];
       float p[4 * NSUB];
 #pragma unroll
