@@ -37,7 +37,8 @@
 //     only tiles that cross a wave's first query carry the causal mask (the
 //     masked scores are set to -inf), tiles past its last query are skipped, and
 //     the running max is raised lazily (see compute()) so the accumulators
-//     are rescaled only on the few tiles that need it.
+//     are rescaled, and the cross-row max taken, only on the few tiles that
+//     need it.
 // P is rounded to the input type for the P.V product; for bf16 it is split
 // into a bf16 head and a bf16 remainder (two MFMAs) to keep ~16 bits. A
 // negative scale is applied as |scale| on negated queries (exact: a sign
