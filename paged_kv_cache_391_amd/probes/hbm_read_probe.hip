@@ -1,5 +1,5 @@
 // HBM read-bandwidth probe (measurement tool, not part of the library).
-// Sets the practical ceiling the decode kernel is judged against:
+// Sets the practical ceiling the decode kernel is measured against:
 //   (a) contiguous streaming reads of 2 GiB, 16-byte loads, plain and with
 //       the non-temporal (streaming) cache hint;
 //   (b) reads of 4 KiB K and V tiles, the access pattern of a paged KV cache:
