@@ -13,8 +13,9 @@
  *
  * Conventions for every call:
  *  - Tensor pointers are DEVICE pointers owned by the caller. The kernel
- *    calls allocate nothing, keep no pointer after returning, hold no global
- *    mutable state and are safe to call from several host threads. The
+ *    calls allocate nothing, keep no pointer after returning and are safe
+ *    to call from several host threads; the only state they keep is each
+ *    device's compute-unit count, read once (atomically) on first use. The
  *    block allocator (pa_allocator_*) keeps its host-side state in a handle
  *    the caller creates and destroys.
  *  - Work is queued on `stream` and never synchronised; the library never

@@ -1,7 +1,10 @@
 // C ABI: host-side validation and kernel dispatch. No allocation, no device
-// reads, no global mutable state.
+// reads; the only state kept between calls is each device's compute-unit
+// count, read once.
 #include <limits.h>
 #include <math.h>
+
+#include <atomic>
 
 #include "../../include/pagedattn.h"
 #include "pa_internal.h"
@@ -29,6 +32,31 @@ pa_status check_cache_shape(int32_t num_heads, int32_t head_dim, int32_t block_s
 
 int64_t max_parts_for(int32_t max_context_len) {
   return max_context_len <= 0 ? 1 : ceil_div(max_context_len, pa::kPartitionTokens);
+}
+
+// Compute units of the current device (0 if it cannot be read: the caller
+// then keeps its default, and the launch reports the device error). The
+// count is read once per device and kept: it is a fixed property of the
+// hardware, and the attribute query costs host time on every call.
+int device_compute_units() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> known[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = known[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  if (dev >= 0 && dev < kMaxDevices) known[dev].store(cus, std::memory_order_relaxed);
+  return cus;
 }
 
 struct DecodeCall {
@@ -346,7 +374,11 @@ static pa_status prepare_prefill(PrefillCall& call, void* out, pa_dtype out_dtyp
     a.scale_log2 = std::fabs(scale) * 1.4426950408889634f;
     a.q_sign = std::signbit(scale) ? 0x80008000u : 0u;
     a.out_f32 = out_dtype == PA_F32 ? 1 : 0;
-    if ((int64_t)a.q_tiles * num_heads * num_seqs > INT32_MAX) return PA_ERR_INVALID_ARG;
+    if ((int64_t)a.q_tiles * num_heads * (num_seqs + 7) > INT32_MAX) return PA_ERR_INVALID_ARG;
+    // more workgroups than the chip holds at once: group each pair's query
+    // tiles for L2 reuse (the kernel's work-order note)
+    const int cus = device_compute_units();
+    a.grouped = cus > 0 && (int64_t)a.q_tiles * num_heads * num_seqs > (int64_t)cus * pa::kPrefillWorkgroupsPerCU;
     return PA_OK;
   }
   // fp32: every query row is a decode over its own causal prefix

@@ -116,11 +116,14 @@ struct PrefillArgs {
   int max_blocks;
   int max_context_len;
   int q_tiles;                      // grid: q tiles per sequence
+  int grouped;                      // grid order: query tiles of a (sequence, head) pair together
   float scale_log2;                 // |scale| * log2(e)
   uint32_t q_sign;                  // 0x80008000 for a negative scale (queries negated), else 0
   int out_f32;
 };
 hipError_t launch_prefill_mfma(const PrefillArgs& a, Dt dt, int D, int BS, hipStream_t stream);
 int prefill_mfma_q_tile();
+// workgroups of the prefill kernel resident at once on each compute unit
+constexpr int kPrefillWorkgroupsPerCU = 3;
 
 }  // namespace pa

@@ -163,12 +163,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   const int n16 = lane & 15;
   const int g4 = lane >> 4;
 
-  int bid = blockIdx.x;
-  const int h = bid % a.H;
-  bid /= a.H;
-  const int s = bid % a.num_seqs;
-  bid /= a.num_seqs;
-  const int qt = a.q_tiles - 1 - bid;  // latest (heaviest) query tiles are dispatched first
+  // Work order. With more workgroups than fit on the chip at once, the
+  // (sequence, head) pairs go in groups of 8: bid = x + 8 (qi + q_tiles grp),
+  // pair = 8 grp + x. Workgroups go round-robin over the 8 XCDs, so all
+  // query tiles of a pair land on one XCD one after another and walk the
+  // same keys together while the K/V tiles sit in that XCD's L2 (each K/V
+  // byte then leaves HBM about once instead of once per query tile).
+  // Otherwise every workgroup is resident at once and the latest (heaviest)
+  // query tiles of all pairs go first, each to its own compute unit.
+  int h, s, qt;
+  if (a.grouped) {
+    const int x = blockIdx.x & 7;
+    const int rest = blockIdx.x >> 3;
+    const int pair = (rest / a.q_tiles) * 8 + x;
+    if (pair >= a.num_seqs * a.H) return;
+    h = pair % a.H;
+    s = pair / a.H;
+    qt = a.q_tiles - 1 - rest % a.q_tiles;
+  } else {
+    int bid = blockIdx.x;
+    h = bid % a.H;
+    bid /= a.H;
+    s = bid % a.num_seqs;
+    bid /= a.num_seqs;
+    qt = a.q_tiles - 1 - bid;
+  }
   const int q_beg = a.query_start_loc[s];
   const int L = a.query_start_loc[s + 1] - q_beg;
   const int j0 = qt * QT;
@@ -472,7 +491,8 @@ int prefill_mfma_q_tile() { return QT; }
 
 template <Dt DT, int D, int BS>
 static hipError_t launch_k4(const PrefillArgs& a, hipStream_t stream) {
-  const int64_t grid = (int64_t)a.q_tiles * a.num_seqs * a.H;
+  const int64_t pairs = (int64_t)a.num_seqs * a.H;
+  const int64_t grid = (int64_t)a.q_tiles * (a.grouped ? (pairs + 7) / 8 * 8 : pairs);
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL((prefill_mfma_kernel<DT, D, BS>), dim3((unsigned)grid), dim3(256), 0, stream, a);
   return hipGetLastError();

@@ -542,6 +542,43 @@ def test_prefill_long_context_and_wide_scores(dtype, scale):
     assert err <= ATOL[dtype], f"prefill max abs err {err:.3e}"
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefill_many_workgroups_grouped_order(dtype):
+    """More query tiles than the chip holds at once (15 chunks x 13 heads x 4
+    tiles of 128 queries = 780 workgroups, more than 3 per compute unit): the
+    kernel then dispatches the query tiles of each (sequence, head) pair
+    together, in groups of 8 pairs (195 pairs leave a partial group). Sampled
+    rows against the oracle, and the first two chunks bit-identical to a call
+    that holds only them (104 workgroups, every one resident at once: the
+    plain order)."""
+    rng = np.random.default_rng(11)
+    prior = [int(x) for x in rng.integers(0, 600, 15)]
+    chunk = [int(x) for x in rng.integers(385, 513, 15)]
+    chunk[0] = 512
+    maxb = math.ceil(max(a + b for a, b in zip(prior, chunk)) / 16)
+    wl = prefill_workload(f"pf_grouped_{dtype}", 706, dtype, 13, 128, 16, prior, chunk, maxb=maxb, pool_factor=1.1)
+    od = _on_device_written(wl)
+    p = wl.prefill
+    kc, vc = oracle.reshape_and_cache(wl.new.k, wl.new.v, wl.k_cache, wl.v_cache, wl.new.slot_mapping, 16, dtype)
+    out32 = host(od.prefill(torch.float32))
+    got = out32.astype(np.float64)
+    assert np.isfinite(got).all()
+    rows = np.concatenate([rng.integers(0, p.total_q, size=1500), p.query_start_loc[:-1], p.query_start_loc[1:] - 1])
+    heads = rng.integers(0, wl.num_heads, size=rows.shape[0])
+    ref = oracle.prefill(p.q, kc, vc, p.block_tables, p.context_lens, p.query_start_loc, wl.scale, dtype,
+                         rows=np.stack([rows, heads], 1))
+    err = np.abs(got[rows, heads] - ref).max()
+    assert err <= ATOL[dtype], f"prefill max abs err {err:.3e}"
+    n2 = int(p.query_start_loc[2])
+    sub = torch.empty((n2, wl.num_heads, wl.head_dim), dtype=torch.float32, device="cuda")
+    pa.paged_attention_prefill(sub, od.pf_q[:n2], od.k_cache, od.v_cache, od.pf_block_tables[:2],
+                               od.pf_context_lens[:2], od.pf_qsl[:3], wl.scale, max_q_len=p.max_q_len,
+                               max_context_len=p.max_context_len)
+    assert np.array_equal(bits(host(sub)), bits(out32[:n2]))
+    outn = od.prefill(TORCH_DT[dtype])
+    assert np.array_equal(bits(host(outn)), bits(rne(out32, dtype)))
+
+
 def test_prefill_config5_sampled_rows_and_decode():
     wl, kc_ref, vc_ref = _config(5)
     od = _on_device_written(wl)
