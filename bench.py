@@ -39,6 +39,7 @@ reported next to it); cpu_baseline = the fp64 oracle on the host cores over
 the same work, and on one thread over a sample of it.
 """
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -56,7 +57,8 @@ MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # dense fp16/bf16 matrix-cor
 KERNEL_SOURCES = ["pa_decode.hip", "pa_decode_device.h", "pa_device.h", "pa_internal.h"]
 SHARED_KERNEL_SOURCES = KERNEL_SOURCES + ["pa_shared.hip"]
 PREFILL_KERNEL_SOURCES = ["pa_prefill.hip", "pa_device.h", "pa_internal.h"]
-LEAD_CYCLES = 2_000_000  # GPU spin before each cold step (gpu_lead)
+LEAD_CYCLES = 4_000_000  # GPU spin before each cold step (gpu_lead), ~2 ms
+WARM_LEAD_CYCLES_PER_STEP = 1_000_000  # spin before the back-to-back eager pass, per step queued behind it
 CPU_SECONDS = 10.0  # the oracle repeats its pass until about this much CPU time has elapsed
 
 WORKLOADS = {
@@ -101,12 +103,13 @@ def kernel_source_hash(shared=False, workload=None):
     return h.hexdigest()
 
 
-def gpu_lead():
-    """Queue a short GPU spin (~1 ms) ahead of a cold step: the host then
-    queues the step's launches while the GPU is still busy, so no event pair
-    around a kernel can include GPU idle time spent waiting for the host."""
+def gpu_lead(cycles=None):
+    """Queue a GPU spin (LEAD_CYCLES, ~1 ms, by default) ahead of timed
+    launches: the host queues them while the GPU is still busy, so no event
+    pair around a kernel can include GPU idle time spent waiting for the
+    host."""
     import torch
-    torch.cuda._sleep(LEAD_CYCLES)
+    torch.cuda._sleep(LEAD_CYCLES if cycles is None else cycles)
 
 
 def log(*a):
@@ -363,11 +366,11 @@ def prefill_main(args):
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
+    gpu_lead(WARM_LEAD_CYCLES_PER_STEP * args.steps)  # the host queues the whole pass before the GPU starts it
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
-    eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    eager_ms = evs[0][0].elapsed_time(evs[-1][-1]) / args.steps  # GPU span of the back-to-back steps
     cw_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     pf_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     eager_out = out.clone()
@@ -517,6 +520,9 @@ def main():
             "heads with no collective in the timed region, so only --gpus 1 is measured.")
         sys.exit(2)
 
+    # no garbage-collection pause of the host inside the timed launches
+    gc.collect()
+    gc.disable()
     if args.workload == "prefill_long":
         if args.block_size is not None or args.plain:
             raise SystemExit("--block-size and --plain do not apply to prefill_long")
@@ -608,11 +614,11 @@ def main():
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    gpu_lead(WARM_LEAD_CYCLES_PER_STEP * args.steps)  # the host queues the whole pass before the GPU starts it
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
-    eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    eager_ms = evs[0][0].elapsed_time(evs[-1][-1]) / args.steps  # GPU span of the back-to-back steps
 
     def phase_ms(a, b):
         return sum(e[a].elapsed_time(e[b]) for e in evs) / args.steps
