@@ -57,6 +57,51 @@ def test_prefill_work_by_hand():
     assert byts == 5 * 1 * 4 * 2 * 2 + 2 * 3 * 1 * 4 * 2
 
 
+def _counter_csv(path, rows):
+    os.makedirs(path, exist_ok=True)
+    with open(os.path.join(path, "bench_counter_collection.csv"), "w") as f:
+        f.write("Kernel_Name,Counter_Name,Counter_Value\n")
+        for name, value in rows:
+            f.write(f'"{name}",X,{value}\n')
+    return path
+
+
+@pytest.mark.parametrize("workload,shared,kernel", [
+    ("llama7b", False, "void pa::decode_partition_kernel<(pa::Dt)1, 128, 16, 1, (pa::RowMode)0>(pa::DecodeArgs)"),
+    ("prefix13b", True, "void pa::shared_prefix_step_kernel<(pa::Dt)1, 128, 16>(pa::DecodeArgs, int)"),
+    ("prefill_long", False, "void pa::prefill_mfma_kernel<(pa::Dt)1, 128, 16>(pa::PrefillArgs)")])
+def test_traffic_record_scales_counters_by_the_plain_copy(tmp_path, monkeypatch, workload, shared, kernel):
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the recorded kernel,
+    each scaled by what the same counter reads for the plain copy of known
+    size, averaged over its dispatches; stamped with the hash of the sources
+    the kernel is built from. Other kernels in the run are ignored."""
+    copy_bytes = 1 << 30
+    other = "pa::reshape_and_cache_kernel(int)"
+    fetch = _counter_csv(str(tmp_path / "f"), [(kernel, 1000.0), (kernel, 3000.0), (other, 9e9),
+                                               ("__amd_rocclr_copyBuffer", 524288.0), ("__amd_rocclr_copyBuffer", 10.0)])
+    write = _counter_csv(str(tmp_path / "w"), [(kernel, 40.0), (kernel, 60.0), (other, 9e9),
+                                               ("__amd_rocclr_copyBuffer", 1048576.0)])
+    out = tmp_path / "rec.json"
+    monkeypatch.setattr(bench, "traffic_file", lambda w, s=False: str(out))
+    bench.record_traffic(workload, shared, fetch, write, copy_bytes)
+    rec = json.load(open(out))
+    assert rec["fetch_bytes_per_launch"] == round(2000.0 * 1024 * 2.0)  # the copy's FETCH reads half its bytes
+    assert rec["write_bytes_per_launch"] == round(50.0 * 1024 * 1.0)
+    assert rec["hbm_bytes_per_launch"] == rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    assert rec["kernel_source_sha256"] == bench.kernel_source_hash(shared, workload)
+    assert rec["kernel"] == bench.traffic_kernel(shared, workload)
+
+
+def test_traffic_records_name_the_roofline_kernels():
+    assert bench.traffic_kernel(False) == "decode_partition_kernel"
+    assert bench.traffic_kernel(True) == "shared_prefix_step_kernel"
+    assert bench.traffic_kernel(False, "prefill_long") == "prefill_mfma_kernel"
+    assert bench.kernel_source_hash(False, "prefill_long") != bench.kernel_source_hash(False)
+    assert bench.traffic_file("prefill_long").endswith("prefill_long_traffic.json")
+    assert bench.traffic_file("prefix13b", True).endswith("decode_prefix13b_shared_traffic.json")
+    assert bench.traffic_file("prefix13b", False).endswith("decode_prefix13b_plain_traffic.json")
+
+
 @pytest.mark.gpu
 def test_bench_prints_one_json_line_with_the_contract():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "3", "--warmup", "1",
