@@ -64,16 +64,44 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(const DecodeArgs a) {
   const int64_t prow = ((int64_t)row * a.H + h) * a.ws_parts;
   const float* ml = a.ws + (int64_t)a.num_rows * a.H * a.ws_parts * D + prow * 2;
   const float* acc = a.ws + prow * D;
-  float M = -INFINITY;
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, ml[2 * p]);
-  float Lsum = 0.f;
-  for (int p = 0; p < nparts; ++p) Lsum += ml[2 * p + 1] * fast_exp2(ml[2 * p] - M);
   constexpr int PER = D / 64;
+  // Every load is issued before any result is needed: lane p reads
+  // partition p's (m, l) and the first PRE partitions' accumulators are read
+  // at once (indices clamped to the row's partitions, weights zero past
+  // them), so the merge waits on memory about once instead of once per
+  // partition. M and L are butterfly reductions across the wave; the
+  // weighted sum of the accumulators runs in partition order.
+  constexpr int PRE = 8;
+  float xa[PRE][PER];
+#pragma unroll
+  for (int p = 0; p < PRE; ++p)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) xa[p][i] = acc[(int64_t)min(p, nparts - 1) * D + lane + 64 * i];
+  const int pl = min(lane, nparts - 1);
+  const float m_l = ml[2 * pl];
+  const float l_l = ml[2 * pl + 1];
+  float M = lane < nparts ? m_l : -INFINITY;
+  for (int p = lane + 64; p < nparts; p += 64) M = fmaxf(M, ml[2 * p]);
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) M = fmaxf(M, shfl_xor_f(M, s));
+  const float w_l = lane < nparts ? fast_exp2(m_l - M) : 0.f;  // weight of partition `lane`
+  float Lsum = l_l * w_l;
+  for (int p = lane + 64; p < nparts; p += 64) Lsum += ml[2 * p + 1] * fast_exp2(ml[2 * p] - M);
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) Lsum += shfl_xor_f(Lsum, s);
   float x[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) x[i] = 0.f;
-  for (int p = 0; p < nparts; ++p) {
-    const float w = fast_exp2(ml[2 * p] - M);
+#pragma unroll
+  for (int p = 0; p < PRE; ++p) {
+    const float w = p < nparts ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_l), p))
+                               : 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) x[i] += xa[p][i] * w;
+  }
+  for (int p = PRE; p < nparts; ++p) {
+    const float w = p < 64 ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_l), p))
+                           : fast_exp2(ml[2 * p] - M);
 #pragma unroll
     for (int i = 0; i < PER; ++i) x[i] += acc[(int64_t)p * D + lane + 64 * i] * w;
   }
