@@ -143,7 +143,7 @@ static hipError_t dispatch_k2_mode(const DecodeArgs& a, int D, int BS, RowMode m
   switch (mode) {
     case RowMode::Decode: return dispatch_k2<DT, RowMode::Decode>(a, D, BS, stream);
     case RowMode::PrefillRows: return dispatch_k2<DT, RowMode::PrefillRows>(a, D, BS, stream);
-    case RowMode::SharedTail: return dispatch_k2<DT, RowMode::SharedTail>(a, D, BS, stream);
+    case RowMode::SharedTail: break;  // tails run inside the shared-prefix step kernel only
   }
   return hipErrorInvalidValue;
 }

@@ -154,13 +154,20 @@ __device__ __forceinline__ void prefill_row(const int32_t* qsl, const int32_t* c
 }
 
 // Group g of a prefix-sharing batch is rows group_starts[g] .. group_starts[g+1]-1.
+// The starts are non-decreasing from group_starts[0] = 0, so the group is
+// the number of starts g >= 1 at or before row r. The wave counts them 64 at
+// a time (lane i reads start g0 + i, one ballot): one memory round trip for
+// up to 65 groups, where a binary search chains log2(groups) loads.
+// Called by whole waves (every lane active).
 __device__ __forceinline__ int group_of_row(const int32_t* group_starts, int num_groups, int r) {
-  int lo = 0, hi = num_groups - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (group_starts[mid] <= r) lo = mid; else hi = mid - 1;
+  const int lane = __lane_id();
+  int cnt = 0;
+  for (int g0 = 1; g0 < num_groups; g0 += 64) {
+    const int g = g0 + lane;
+    const bool before = g < num_groups && group_starts[min(g, num_groups - 1)] <= r;
+    cnt += __popcll(__ballot(before));
   }
-  return lo;
+  return cnt;
 }
 
 // Partition layout of one row: own partitions cover tokens [tok0, ctx) in
