@@ -178,6 +178,21 @@ def test_decode_ragged_lengths(dtype, D, bs):
     _check_attention(od.decode(torch.float32, split=False), ref, dtype)
 
 
+def test_decode_rows_of_many_partitions():
+    """The reduction reads the first 8 partitions' accumulators at once and
+    holds one partition's (m, l) per lane: rows of 8 and 9 partitions (the
+    first boundary) and of 64, 65 and 66 (past one value per lane)."""
+    P = pa.decode_partition_tokens()
+    ctx = [8 * P, 8 * P + 1, 9 * P, 64 * P, 64 * P + 100, 65 * P + 7]
+    wl = decode_workload("many_parts", 611, "f16", 2, 128, 16, ctx, maxb=math.ceil(max(ctx) / 16), pool_factor=1.05)
+    od = _on_device_written(wl)
+    kc, vc = oracle.reshape_and_cache(wl.new.k, wl.new.v, wl.k_cache, wl.v_cache, wl.new.slot_mapping, 16, "f16")
+    d = wl.decode
+    ref = oracle.decode(d.q, kc, vc, d.block_tables, d.context_lens, wl.scale, "f16")
+    _check_attention(od.decode(torch.float32, split=True), ref, "f16")
+    _check_attention(od.decode(torch.float32, split=False), ref, "f16")
+
+
 def test_decode_empty_context_gives_zeros():
     wl = decode_workload("empty", 601, "f16", 2, 128, 16, [0, 5, 0, 40], maxb=4, pool_blocks=8)
     od = _on_device_written(wl)
@@ -440,6 +455,26 @@ def test_shared_prefix_decode_ragged_groups(dtype, bs):
     pa.paged_attention_decode_shared_prefix(again, dq, dk, dv, dev(bt), dev(ctx), dev(gs), dev(pl), scale, maxctx,
                                             int(np.diff(gs).max()), int(pl.max()), ws)
     assert torch.equal(out, again)
+
+
+def test_shared_prefix_decode_more_groups_than_a_wave_has_lanes():
+    """70 prefix-sharing groups: a row finds its group by counting the group
+    starts at or before it, 64 starts per ballot, so this takes two."""
+    rng = np.random.default_rng(70)
+    groups = []
+    for i in range(70):
+        n = 1 + i % 3
+        groups.append((n, 16 * (i % 5), [int(t) for t in rng.integers(0, 40, n)]))
+    kc, vc, q, bt, ctx, gs, pl = _grouped_batch("f16", 16, groups, 77)
+    H, D = q.shape[1], q.shape[2]
+    scale = 1 / math.sqrt(D)
+    ref = oracle.decode(q, kc, vc, bt, ctx, scale, "f16")
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    maxctx = int(ctx.max())
+    ws = pa.make_decode_shared_workspace(len(ctx), H, D, maxctx)
+    pa.paged_attention_decode_shared_prefix(out, dev(q, "f16"), dev(kc, "f16"), dev(vc, "f16"), dev(bt), dev(ctx),
+                                            dev(gs), dev(pl), scale, maxctx, int(np.diff(gs).max()), int(pl.max()), ws)
+    _check_attention(out, ref, "f16")
 
 
 # ----------------------------------------------------------------- prefill
