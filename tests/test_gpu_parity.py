@@ -577,8 +577,9 @@ def test_prefill_long_context_and_wide_scores(dtype, scale):
     assert err <= ATOL[dtype], f"prefill max abs err {err:.3e}"
 
 
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_prefill_many_workgroups_grouped_order(dtype):
+@pytest.mark.parametrize("dtype,D,bs", [("f16", 128, 16), ("bf16", 128, 16), ("f16", 64, 32), ("bf16", 128, 64),
+                                        ("f16", 128, 8)])
+def test_prefill_many_workgroups_grouped_order(dtype, D, bs):
     """More query tiles than the chip holds at once (15 chunks x 13 heads x 4
     tiles of 128 queries = 780 workgroups, more than 3 per compute unit): the
     kernel then dispatches the query tiles of each (sequence, head) pair
@@ -590,11 +591,12 @@ def test_prefill_many_workgroups_grouped_order(dtype):
     prior = [int(x) for x in rng.integers(0, 600, 15)]
     chunk = [int(x) for x in rng.integers(385, 513, 15)]
     chunk[0] = 512
-    maxb = math.ceil(max(a + b for a, b in zip(prior, chunk)) / 16)
-    wl = prefill_workload(f"pf_grouped_{dtype}", 706, dtype, 13, 128, 16, prior, chunk, maxb=maxb, pool_factor=1.1)
+    maxb = math.ceil(max(a + b for a, b in zip(prior, chunk)) / bs)
+    wl = prefill_workload(f"pf_grouped_{dtype}_{D}_{bs}", 706 + bs, dtype, 13, D, bs, prior, chunk, maxb=maxb,
+                          pool_factor=1.1)
     od = _on_device_written(wl)
     p = wl.prefill
-    kc, vc = oracle.reshape_and_cache(wl.new.k, wl.new.v, wl.k_cache, wl.v_cache, wl.new.slot_mapping, 16, dtype)
+    kc, vc = oracle.reshape_and_cache(wl.new.k, wl.new.v, wl.k_cache, wl.v_cache, wl.new.slot_mapping, bs, dtype)
     out32 = host(od.prefill(torch.float32))
     got = out32.astype(np.float64)
     assert np.isfinite(got).all()
