@@ -616,6 +616,30 @@ def test_prefill_many_workgroups_grouped_order(dtype, D, bs):
     assert np.array_equal(bits(host(outn)), bits(rne(out32, dtype)))
 
 
+def test_prefill_bench_workload_sampled_rows():
+    """bench.py's compute-bound prefill (8 chunks of 512 queries after 1536
+    cached tokens, 40 heads: 1280 workgroups, the grouped order) in the
+    launch configuration it times: sampled rows against the oracle, and the
+    output in the input type equal to the rounded f32 output."""
+    import bench
+    wl = bench.prefill_config()
+    od = _on_device_written(wl)
+    p = wl.prefill
+    kc, vc = oracle.reshape_and_cache(wl.new.k, wl.new.v, wl.k_cache, wl.v_cache, wl.new.slot_mapping,
+                                      wl.block_size, wl.dtype)
+    out32 = host(od.prefill(torch.float32))
+    rng = np.random.default_rng(397)
+    rows = np.concatenate([rng.integers(0, p.total_q, size=1500), p.query_start_loc[:-1], p.query_start_loc[1:] - 1])
+    heads = rng.integers(0, wl.num_heads, size=rows.shape[0])
+    ref = oracle.prefill(p.q, kc, vc, p.block_tables, p.context_lens, p.query_start_loc, wl.scale, wl.dtype,
+                         rows=np.stack([rows, heads], 1))
+    err = np.abs(out32[rows, heads].astype(np.float64) - ref).max()
+    print(f"prefill_long sampled max abs err {err:.3e}")
+    assert err <= ATOL[wl.dtype]
+    outn = od.prefill(TORCH_DT[wl.dtype])
+    assert np.array_equal(bits(host(outn)), bits(rne(out32, wl.dtype)))
+
+
 def test_prefill_config5_sampled_rows_and_decode():
     wl, kc_ref, vc_ref = _config(5)
     od = _on_device_written(wl)
