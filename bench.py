@@ -109,7 +109,8 @@ def gpu_lead(cycles=None):
     pair around a kernel can include GPU idle time spent waiting for the
     host."""
     import torch
-    torch.cuda._sleep(LEAD_CYCLES if cycles is None else cycles)
+    if hasattr(torch.cuda, "_sleep"):  # a private helper of torch: without it, no lead
+        torch.cuda._sleep(LEAD_CYCLES if cycles is None else cycles)
 
 
 def log(*a):
