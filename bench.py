@@ -479,7 +479,8 @@ def prefill_main(args):
                      "flops_per_launch": flops, "bytes_per_launch": pf_bytes,
                      "avg_launch_us": round(cold_ms * 1e3, 2),
                      "timing": f"HIP events on the launch stream around each of {args.steps} eager launches, "
-                               f"each after a {args.evict_mib} MiB {args.evict_mode} that evicts L2 and MALL",
+                               f"each after a GPU spin (the launches queued ahead) and a {args.evict_mib} MiB "
+                               f"{args.evict_mode} that evicts L2 and MALL",
                      "launch_us": pct(cold_pf), "warm_avg_launch_us": round(pf_ms * 1e3, 2),
                      "hbm_frac": round(pf_bytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                      "roofline_us": round(max(flops / (peak * 1e12), pf_bytes / (HBM_PEAK_GBPS * 1e9)) * 1e6, 2)},
@@ -765,7 +766,8 @@ def main():
                                 else f"decode_partition_kernel<{wl.dtype},{D},{bs}>"),
                      "bytes_per_launch": k2_bytes, "avg_launch_us": round(k2_cold_ms * 1e3, 2),
                      "timing": f"HIP events on the launch stream around each of {args.steps} eager launches, "
-                               f"each after a {args.evict_mib} MiB {args.evict_mode} that evicts L2 and MALL",
+                               f"each after a GPU spin (the launches queued ahead) and a {args.evict_mib} MiB "
+                               f"{args.evict_mode} that evicts L2 and MALL",
                      "launch_us": pct(cold_k2), "warm_avg_launch_us": round(k2_ms * 1e3, 2),
                      "warm_GBps": round(k2_warm_gbps, 1)},
         "timing": ("hip_graph_replay" + (" of pa_attention_step (prefill on a side stream, concurrent with the "
