@@ -52,6 +52,31 @@ def test_reshape_and_cache_bit_exact(cid):
     assert np.array_equal(bits(host(od.v_cache)), bits(vc_ref))
 
 
+@pytest.mark.parametrize("dtype,H,D,bs", [("f16", 4, 128, 16), ("bf16", 2, 64, 32), ("f32", 3, 128, 8),
+                                          ("f16", 5, 64, 64)])
+def test_reshape_and_cache_padding_and_slots_past_the_pool(dtype, H, D, bs):
+    """Rows with a negative slot (padding) and rows whose slot lies past the
+    pool are skipped; every other row lands bit-exactly in its slot, and every
+    slot no row names keeps its poison bits."""
+    from workloads import normal, poison_array
+    rng = np.random.default_rng(17 + bs)
+    T = 200
+    nb = -(-T // bs) + 8  # room for every row, and slots no row names
+    slots = rng.permutation(nb * bs)[:T].astype(np.int32)
+    slots[rng.random(T) < 0.2] = -1
+    past = rng.choice(T, 5, replace=False)
+    slots[past] = nb * bs + rng.integers(0, 1000, 5)
+    k, v = normal(rng, (T, H, D), dtype), normal(rng, (T, H, D), dtype)
+    kc, vc = poison_array((nb, H, bs, D), dtype), poison_array((nb, H, bs, D), dtype)
+    dk, dv = dev(kc, dtype), dev(vc, dtype)
+    pa.reshape_and_cache(dev(k, dtype), dev(v, dtype), dk, dv, dev(slots))
+    valid = slots.copy()
+    valid[past] = -1
+    kr, vr = oracle.reshape_and_cache(k, v, kc, vc, valid, bs, dtype)
+    assert np.array_equal(bits(host(dk)), bits(kr))
+    assert np.array_equal(bits(host(dv)), bits(vr))
+
+
 @pytest.mark.parametrize("dtype,H,D,bs", [("f16", 40, 128, 16), ("bf16", 32, 128, 32), ("f32", 2, 64, 16),
                                           ("f16", 8, 128, 8), ("bf16", 4, 64, 64)])
 def test_copy_blocks_bit_exact(dtype, H, D, bs):
