@@ -525,6 +525,22 @@ def test_prefill_parity_small_chunks(dtype, bs):
         assert np.array_equal(bits(host(outn)), bits(rne(host(out32), dtype)))
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+def test_prefill_empty_chunks_between_others(dtype):
+    """Chunks of no queries (equal neighbours in query_start_loc) in the
+    middle and at the end of the batch: their workgroups do nothing and the
+    other chunks' rows are unaffected."""
+    wl = prefill_workload(f"pf_empty_{dtype}", 712, dtype, 3, 128, 16, [40, 300, 0, 77, 5, 9],
+                          [33, 0, 20, 0, 140, 0], maxb=24, pool_factor=1.2)
+    od = _on_device_written(wl)
+    p = wl.prefill
+    kc, vc = oracle.reshape_and_cache(wl.new.k, wl.new.v, wl.k_cache, wl.v_cache, wl.new.slot_mapping, 16, dtype)
+    ref = oracle.prefill(p.q, kc, vc, p.block_tables, p.context_lens, p.query_start_loc, wl.scale, dtype)
+    got = host(od.prefill(torch.float32)).astype(np.float64)
+    assert got.shape == ref.shape
+    assert np.abs(got - ref).max() <= ATOL[dtype]
+
+
 @pytest.mark.parametrize("dtype,bs", [("f16", 8), ("bf16", 16), ("f16", 64)])
 def test_prefill_head_dim_64(dtype, bs):
     """head_dim 64: a wave's V rows of one load span two 8-token blocks at
