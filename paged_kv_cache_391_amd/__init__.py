@@ -30,7 +30,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = 0, -1, -2, -3, -4
-PA_ERR_NO_BLOCKS, PA_ERR_NO_MEMORY = -5, -6
+PA_ERR_NO_BLOCKS, PA_ERR_NO_MEMORY, PA_ERR_PENDING_WRITES = -5, -6, -7
 _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 _lib = None
 
@@ -244,15 +244,15 @@ class BlockAllocator:
 
     def take_copies(self):
         """Pending copy-on-write (src, dst) block pairs, oldest first, as an
-        int32 ``[n, 2]`` numpy array; the queue is emptied."""
+        int32 ``[n, 2]`` numpy array; the queue is emptied and the open batch
+        closed (queue these copies, then the batch's cache writes)."""
         import numpy as np
         n = ctypes.c_int32()
         _check("allocator_take_copies", lib().pa_allocator_take_copies(self._h, None, 0, ctypes.byref(n)))
-        out = np.zeros((n.value, 2), dtype=np.int32)
-        if n.value:
-            _check("allocator_take_copies", lib().pa_allocator_take_copies(
-                self._h, out.ctypes.data_as(ctypes.c_void_p), n.value, ctypes.byref(n)))
-        return out
+        buf = np.zeros((max(1, n.value), 2), dtype=np.int32)  # capacity > 0 closes the batch
+        _check("allocator_take_copies", lib().pa_allocator_take_copies(
+            self._h, buf.ctypes.data_as(ctypes.c_void_p), buf.shape[0], ctypes.byref(n)))
+        return buf[:n.value].copy()
 
 
 def gather_kv(k_out, v_out, k_cache, v_cache, block_tables, context_lens, cu_context_lens, max_context_len: int):

@@ -16,6 +16,22 @@
 // on are queued as (src, dst) block pairs that the caller hands to
 // pa_copy_blocks before writing the new tokens with pa_reshape_and_cache.
 // Free blocks are a LIFO stack that first hands out block 0, 1, 2, ...
+//
+// Batches. The allocator's calls of one scheduler step form a batch that
+// take_copies closes once it has handed out every pending pair; the caller
+// then queues the batch's copies and, after them, its cache writes. Within a
+// batch the copies run concurrently and before any of the batch's writes, so
+// the allocator keeps two rules that make every batch safe to run that way:
+//   * a block that received slots in the current batch (its new tokens are
+//     not written yet, or it is a copy destination) is never a copy source:
+//     an append that would copy it returns PA_ERR_PENDING_WRITES and changes
+//     nothing (close the batch, queue its work, then append again);
+//   * a block whose count drops to 0 while it received slots or is a copy
+//     source in the current batch returns to the pool only when the batch
+//     closes, so it is neither a destination of the same batch's copies nor
+//     handed a second set of slots in the same batch.
+// Together: a batch's destinations are distinct fresh blocks, none is a
+// source, and every source holds its final contents when the copies run.
 #include <limits.h>
 
 #include <new>
@@ -35,6 +51,10 @@ struct pa_allocator {
   std::vector<int32_t> refcount;
   std::vector<Seq> seqs;
   std::vector<int32_t> copies;      // pending (src, dst) pairs, flattened
+  int64_t batch = 0;                // number of the open batch
+  std::vector<int64_t> filled_in;   // batch in which the block last received slots (-1: never)
+  std::vector<int64_t> source_in;   // batch in which the block was last a copy source (-1: never)
+  std::vector<int32_t> deferred;    // blocks freed in the open batch, returned when it closes
 };
 
 namespace {
@@ -51,7 +71,19 @@ int32_t take_block(pa_allocator* a) {
 }
 
 void release_block(pa_allocator* a, int32_t b) {
-  if (--a->refcount[b] == 0) a->free_stack.push_back(b);
+  if (--a->refcount[b] != 0) return;
+  if (a->filled_in[b] == a->batch || a->source_in[b] == a->batch)
+    a->deferred.push_back(b);  // the open batch still writes or reads it
+  else
+    a->free_stack.push_back(b);
+}
+
+// Close the open batch: blocks freed during it return to the pool (in the
+// order they were freed), and every block becomes a valid copy source.
+void close_batch(pa_allocator* a) {
+  for (int32_t b : a->deferred) a->free_stack.push_back(b);
+  a->deferred.clear();
+  ++a->batch;
 }
 
 // Blocks an append of n tokens to s takes from the pool: fresh blocks for
@@ -86,6 +118,10 @@ pa_status pa_allocator_create(int32_t num_blocks, int32_t block_size, pa_allocat
     a->num_blocks = num_blocks;
     a->block_size = block_size;
     a->refcount.assign(num_blocks, 0);
+    a->filled_in.assign(num_blocks, -1);
+    a->source_in.assign(num_blocks, -1);
+    a->deferred.reserve(num_blocks);  // close_batch and release_block never allocate
+    a->free_stack.reserve(num_blocks);
     a->free_stack.resize(num_blocks);
     for (int32_t i = 0; i < num_blocks; ++i) a->free_stack[i] = num_blocks - 1 - i;
   } catch (const std::bad_alloc&) {
@@ -139,6 +175,12 @@ pa_status pa_allocator_append(pa_allocator* a, int32_t seq, int32_t num_tokens, 
   if (!seq_ok(a, seq) || num_tokens < 0) return PA_ERR_INVALID_ARG;
   pa_allocator::Seq& s = a->seqs[seq];
   if ((int64_t)s.length + num_tokens > INT32_MAX) return PA_ERR_INVALID_ARG;
+  const int32_t bs = a->block_size;
+  // a shared, partly filled last block is copied first: not while the open
+  // batch still has writes into it (they would run after the copy)
+  if (num_tokens > 0 && s.length % bs != 0 && a->refcount[s.table.back()] > 1 &&
+      a->filled_in[s.table.back()] == a->batch)
+    return PA_ERR_PENDING_WRITES;  // nothing changed
   const int64_t need = blocks_needed(a, s, num_tokens);
   if (need > (int64_t)a->free_stack.size()) return PA_ERR_NO_BLOCKS;  // nothing changed
   try {
@@ -147,7 +189,6 @@ pa_status pa_allocator_append(pa_allocator* a, int32_t seq, int32_t num_tokens, 
   } catch (const std::bad_alloc&) {
     return PA_ERR_NO_MEMORY;
   }
-  const int32_t bs = a->block_size;
   for (int32_t i = 0; i < num_tokens; ++i) {
     const int32_t off = s.length % bs;
     if (off == 0) {
@@ -157,9 +198,11 @@ pa_status pa_allocator_append(pa_allocator* a, int32_t seq, int32_t num_tokens, 
       const int32_t fresh = take_block(a);
       a->copies.push_back(old);
       a->copies.push_back(fresh);
+      a->source_in[old] = a->batch;
       release_block(a, old);
       s.table.back() = fresh;
     }
+    a->filled_in[s.table.back()] = a->batch;
     if (slots) slots[i] = s.table.back() * bs + off;
     ++s.length;
   }
@@ -201,6 +244,7 @@ pa_status pa_allocator_take_copies(pa_allocator* a, int32_t* pairs, int32_t capa
   for (int64_t i = 0; i < 2 * n; ++i) pairs[i] = a->copies[i];
   a->copies.erase(a->copies.begin(), a->copies.begin() + 2 * n);
   *num_pairs = (int32_t)n;
+  if (a->copies.empty()) close_batch(a);
   return PA_OK;
 }
 

@@ -127,6 +127,7 @@ const char* pa_status_string(pa_status status) {
     case PA_ERR_HIP: return "HIP launch failure";
     case PA_ERR_NO_BLOCKS: return "no free KV block left in the pool";
     case PA_ERR_NO_MEMORY: return "host memory allocation failed";
+    case PA_ERR_PENDING_WRITES: return "copy source still has writes in the open batch: take_copies first";
   }
   return "unknown status";
 }

@@ -84,6 +84,7 @@ def test_copy_on_write_of_a_shared_partial_block():
     a = pa.BlockAllocator(16, 16)
     parent = a.new_sequence()
     a.append(parent, 37)                      # blocks 0, 1, 2 (block 2 holds 5 tokens)
+    assert a.take_copies().shape == (0, 2)    # close the batch: the prompt's writes are queued
     kids = [a.fork(parent) for _ in range(3)]
     assert [a.refcount(b) for b in range(3)] == [4, 4, 4]
     s0 = a.append(kids[0], 2)                 # block 2 is shared and partly filled: copied first
@@ -127,3 +128,134 @@ def test_native_allocator_errors_change_nothing():
         pa.BlockAllocator(0, 16)
     with pytest.raises(pa.PagedAttnError):
         pa.BlockAllocator(1 << 28, 16)        # slots would overflow int32
+
+
+def test_copy_source_with_writes_in_the_open_batch_is_refused():
+    """new, append 5, fork, append 1 to the parent (its shared block 0 is
+    copied to block 1, which receives the new token), fork the parent, append
+    1 to the new child: copying block 1 now would chain two copies in one
+    batch and miss the parent's token, whose write runs after the copies. The
+    append is refused and changes nothing; once the batch is closed it copies
+    block 1 (by then holding the token) in a batch of its own."""
+    a = pa.BlockAllocator(8, 16)
+    p = a.new_sequence()
+    a.append(p, 5)
+    assert a.take_copies().shape == (0, 2)
+    c1 = a.fork(p)
+    assert a.append(p, 1).tolist() == [16 + 5]
+    c2 = a.fork(p)
+    before = (a.num_free, a.block_table(c2).tolist(), a.length(c2), [a.refcount(b) for b in range(8)])
+    with pytest.raises(pa.PagedAttnError) as e:
+        a.append(c2, 1)
+    assert e.value.status == pa.PA_ERR_PENDING_WRITES
+    assert before == (a.num_free, a.block_table(c2).tolist(), a.length(c2), [a.refcount(b) for b in range(8)])
+    assert a.take_copies().tolist() == [[0, 1]]
+    assert a.append(c2, 1).tolist() == [2 * 16 + 6]
+    assert a.take_copies().tolist() == [[1, 2]]
+    assert a.block_table(c1).tolist() == [0] and a.block_table(p).tolist() == [1] and a.block_table(c2).tolist() == [2]
+
+
+def test_blocks_freed_in_a_batch_return_when_it_closes():
+    """A copy source freed in the open batch (and a block that received
+    slots in it) must not come back as a destination or as fresh slots in
+    the same batch: they rejoin the pool when take_copies closes it."""
+    a = pa.BlockAllocator(4, 16)
+    p = a.new_sequence()
+    a.append(p, 5)                            # block 0
+    a.take_copies()
+    k = a.fork(p)
+    a.append(k, 1)                            # copy 0 -> 1; block 0 is a source in this batch
+    a.free(p)                                 # block 0's count drops to 0: deferred
+    assert a.num_free == 2 and a.refcount(0) == 0
+    q = a.new_sequence()
+    assert a.append(q, 20).tolist()[0] == 2 * 16  # blocks 2 and 3, not 0
+    assert a.take_copies().tolist() == [[0, 1]]
+    assert a.num_free == 1                    # block 0 is back
+    r = a.new_sequence()
+    assert a.append(r, 1).tolist() == [0]
+
+
+def _simulate(bs, nb, seed, steps):
+    """Random allocator traffic with batches closed at random points. Each
+    batch runs the way a caller queues it on one stream: every copy reads its
+    source before any copy writes (they are concurrent), then the batch's
+    cache writes land. Checked after every batch: destinations distinct and
+    never sources, slots of the batch distinct, and every live sequence reads
+    back, through its table, exactly the tokens it holds."""
+    rng = np.random.default_rng(seed)
+    a = pa.BlockAllocator(nb, bs)
+    content = np.full((nb, bs), -1, dtype=np.int64)
+    tokens = {}        # seq id -> its token ids, in order
+    writes = []        # (slot, token) of the open batch
+    next_tok = 0
+    refused = 0
+
+    def close():
+        pairs = a.take_copies()
+        if pairs.size:
+            src, dst = pairs[:, 0], pairs[:, 1]
+            assert len(set(dst.tolist())) == len(dst), "two copies into one block"
+            assert not set(dst.tolist()) & set(src.tolist()), "a destination is also a source"
+            content[dst] = content[src].copy()   # all reads before any write
+        slots = [w[0] for w in writes]
+        assert len(set(slots)) == len(slots), "one slot handed out twice in a batch"
+        for slot, tok in writes:
+            content[slot // bs, slot % bs] = tok
+        writes.clear()
+        for sid, toks in tokens.items():
+            t = a.block_table(sid)
+            got = [int(content[t[i // bs], i % bs]) for i in range(len(toks))]
+            assert got == toks, f"sequence {sid} reads {got} instead of {toks}"
+
+    for _ in range(steps):
+        op = rng.choice(["new", "append", "append", "append", "fork", "fork", "free", "close"])
+        if op == "new" or not tokens:
+            tokens[a.new_sequence()] = []
+        elif op == "append":
+            sid = int(rng.choice(list(tokens)))
+            n = int(rng.integers(1, bs + 2))
+            state = (a.num_free, a.block_table(sid).tolist(), a.length(sid))
+            try:
+                slots = a.append(sid, n)
+            except pa.PagedAttnError as e:
+                assert e.status in (pa.PA_ERR_NO_BLOCKS, pa.PA_ERR_PENDING_WRITES)
+                assert state == (a.num_free, a.block_table(sid).tolist(), a.length(sid))
+                refused += e.status == pa.PA_ERR_PENDING_WRITES
+                continue
+            new = list(range(next_tok, next_tok + n))
+            next_tok += n
+            writes.extend(zip(slots.tolist(), new))
+            tokens[sid] = tokens[sid] + new
+        elif op == "fork":
+            sid = int(rng.choice(list(tokens)))
+            kid = a.fork(sid)
+            tokens[kid] = list(tokens[sid])
+            if rng.random() < 0.5:   # a sample's first token right away: copy-on-write of a fresh block
+                try:
+                    slots = a.append(kid, 1)
+                except pa.PagedAttnError as e:
+                    assert e.status in (pa.PA_ERR_NO_BLOCKS, pa.PA_ERR_PENDING_WRITES)
+                    refused += e.status == pa.PA_ERR_PENDING_WRITES
+                    continue
+                writes.append((int(slots[0]), next_tok))
+                tokens[kid] = tokens[kid] + [next_tok]
+                next_tok += 1
+        elif op == "free":
+            sid = int(rng.choice(list(tokens)))
+            a.free(sid)
+            del tokens[sid]           # its queued writes still land (the caller may have queued them)
+        else:
+            close()
+    close()
+    assert sum(a.refcount(b) for b in range(nb)) == sum(len(a.block_table(s)) for s in tokens)
+    for sid in list(tokens):
+        a.free(sid)
+    a.take_copies()
+    assert a.num_free == nb
+    return refused
+
+
+@pytest.mark.parametrize("bs,seed", [(4, 1), (8, 2), (16, 3), (16, 4)])
+def test_batches_run_safely_as_concurrent_copies_then_writes(bs, seed):
+    refused = _simulate(bs, 64, seed, 3000)
+    assert refused > 0  # the traffic does reach the guarded case
