@@ -5,9 +5,10 @@
 // (linked from oracle/liboracle.so; test code only), then the same three
 // parts as one pa_attention_step (the pa_step_args struct filled from C), in
 // order and with the prefill on a side stream, each equal bit for bit to
-// the separate calls. Prints "max_abs_err <x>", "prefill_max_abs_err <y>"
-// and "step_bit_identical <0|1>"; exits 0 when x, y <= 2e-3 and the step
-// results are identical.
+// the separate calls and within tolerance of the oracle. Prints
+// "max_abs_err <x>", "prefill_max_abs_err <y>", "step_bit_identical <0|1>",
+// "step_max_abs_err <z>" and "step_prefill_max_abs_err <w>"; exits 0 when
+// x, y, z, w <= 2e-3 and the step results are identical.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -243,6 +244,7 @@ int main() {
   HIP_OK(hipEventCreateWithFlags(&fork, hipEventDisableTiming));
   HIP_OK(hipEventCreateWithFlags(&join, hipEventDisableTiming));
   int identical = 1;
+  double step_err = 0.0, step_perr = 0.0;  // the step's outputs against the oracle, worst of both modes
   for (int mode = 0; mode < 2; ++mode) {
     HIP_OK(hipMemsetAsync(dsdec, 0xff, (size_t)S * H * D * 4, stream));
     HIP_OK(hipMemsetAsync(dspf, 0xff, (size_t)TQ * H * D * 4, stream));
@@ -254,6 +256,8 @@ int main() {
     if (std::memcmp(sdec.data(), out.data(), out.size() * 4) != 0 ||
         std::memcmp(spf.data(), pout.data(), pout.size() * 4) != 0)
       identical = 0;
+    for (size_t i = 0; i < sdec.size(); ++i) step_err = std::fmax(step_err, std::fabs((double)sdec[i] - ref[i]));
+    for (size_t i = 0; i < spf.size(); ++i) step_perr = std::fmax(step_perr, std::fabs((double)spf[i] - pref[i]));
   }
   // a side stream equal to the main stream is refused before anything runs
   if (pa_attention_step(&a, stream, stream, fork, join) != PA_ERR_INVALID_ARG) {
@@ -261,5 +265,7 @@ int main() {
     return 4;
   }
   std::printf("step_bit_identical %d\n", identical);
-  return (err <= 2e-3 && perr <= 2e-3 && identical) ? 0 : 1;
+  std::printf("step_max_abs_err %.3e\n", step_err);
+  std::printf("step_prefill_max_abs_err %.3e\n", step_perr);
+  return (err <= 2e-3 && perr <= 2e-3 && identical && step_err <= 2e-3 && step_perr <= 2e-3) ? 0 : 1;
 }

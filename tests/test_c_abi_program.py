@@ -3,7 +3,8 @@ binding, no torch): tests/c_abi/decode_from_c.cpp writes new tokens with
 pa_reshape_and_cache, runs a split-K pa_paged_attention_decode and a causal
 pa_paged_attention_prefill and compares their fp32 outputs with the fp64
 oracle, then runs the same work as one pa_attention_step (in order and with
-a side stream) and checks it equals the separate calls bit for bit."""
+a side stream) and checks it equals the separate calls bit for bit and
+matches the oracle on both outputs."""
 import os
 import subprocess
 
@@ -27,3 +28,5 @@ def test_c_program_matches_the_oracle_and_the_step_call():
     assert float(vals["max_abs_err"]) <= 2e-3
     assert float(vals["prefill_max_abs_err"]) <= 2e-3
     assert vals["step_bit_identical"] == "1"
+    assert float(vals["step_max_abs_err"]) <= 2e-3
+    assert float(vals["step_prefill_max_abs_err"]) <= 2e-3
