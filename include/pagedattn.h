@@ -53,7 +53,8 @@ typedef enum {
   PA_ERR_WORKSPACE = -3,   /* split-K workspace missing or too small */
   PA_ERR_HIP = -4,         /* a launch failed; hipGetLastError() was cleared */
   PA_ERR_NO_BLOCKS = -5,   /* block allocator: not enough free blocks (nothing was changed) */
-  PA_ERR_NO_MEMORY = -6    /* block allocator: host memory allocation failed */
+  PA_ERR_NO_MEMORY = -6,   /* block allocator: host memory allocation failed */
+  PA_ERR_PENDING_WRITES = -7 /* block allocator: the copy source still has writes in the open batch */
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
@@ -123,9 +124,26 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapp
  *                 non-zero capacity is INVALID_ARG
  *   take_copies   moves up to capacity pending (src, dst) pairs into
  *                 pairs[capacity][2], oldest first, and sets *num_pairs;
- *                 capacity 0 only queries how many are pending
+ *                 capacity 0 only queries how many are pending. A call
+ *                 with capacity > 0 that leaves nothing pending closes the
+ *                 open batch (below).
  *   num_free / refcount / sequence_length return -1 for a bad handle, block or id.
- * Errors: INVALID_ARG (null pointer, bad id, size), NO_BLOCKS, NO_MEMORY.
+ *
+ * Batches: the calls of one scheduler step form a batch. Close it with
+ * take_copies (capacity > 0, even when nothing is pending), then queue on
+ * one stream, in this order: pa_copy_blocks of the pairs it returned, then
+ * pa_reshape_and_cache of every slot the batch's appends handed out. The
+ * allocator guarantees that the pairs of one batch have distinct
+ * destinations, that no destination is also a source, and that no source
+ * receives slots in the same batch (so the copies see its final contents):
+ *   - append returns PA_ERR_PENDING_WRITES, changing nothing, when it would
+ *     copy a shared last block that received slots in the open batch (its
+ *     new tokens are not written yet); close the batch and append again;
+ *   - a block whose count drops to 0 while it received slots or is a copy
+ *     source in the open batch returns to the pool when the batch closes
+ *     (num_free counts it from then on).
+ * Errors: INVALID_ARG (null pointer, bad id, size), NO_BLOCKS, NO_MEMORY,
+ * PENDING_WRITES.
  */
 typedef struct pa_allocator pa_allocator;
 pa_status pa_allocator_create(int32_t num_blocks, int32_t block_size, pa_allocator** out);
@@ -143,7 +161,13 @@ pa_status pa_allocator_take_copies(pa_allocator* a, int32_t* pairs, int32_t capa
 
 /*
  * gather_kv -- materialise each sequence's logical K and V contiguously
- * through its block table (the translation every attention kernel uses):
+ * through its block table (the translation every attention kernel uses).
+ * The pages define the translation: each logical page of a sequence maps to
+ * a physical block through a page table, and the kernel stitches the
+ * scattered blocks into the stream attention reads (devpress page, section
+ * "分页式KV缓存：让显存利用接近理论极限"; betteryeah page, section 2.2, pages
+ * stored anywhere and reached through the table). This call performs only
+ * that stitching:
  *   k_out[cu_context_lens[s] + t][h][:] = k_cache[bt[s][t/bs]][h][t%bs][:]
  * for t < context_lens[s]; same for v. Bit-exact copy, for checking the
  * table translation and for debugging.
@@ -159,23 +183,38 @@ pa_status pa_gather_kv(void* k_out, void* v_out, const void* k_cache, const void
                        int32_t max_blocks_per_seq, pa_dtype dtype, hipStream_t stream);
 
 /*
- * Split-K sizing for decode. Contexts are cut into partitions of
- * pa_decode_partition_tokens() tokens (a whole number of blocks). The
- * workspace holds fp32 partials (m, l, acc[head_dim]) for every (sequence,
- * head, partition): pa_decode_workspace_bytes() bytes, or 0 when
- * max_context_len fits one partition (then no workspace is needed).
+ * Split-K sizing for decode. The pages do not describe splitting one
+ * sequence's attention: they only say that long contexts (4K tokens and
+ * more) are where paging pays most (betteryeah page, section 3.3, long
+ * sequences) and configure contexts of up to 4096 tokens (devpress page,
+ * the max_model_len setting in the example after "实际收益远超预期"). Cutting
+ * such contexts into partitions that run in parallel and are merged by a
+ * separate reduction is this library's design for keeping every compute
+ * unit busy when a batch holds few long sequences.
+ * Contexts are cut into partitions of pa_decode_partition_tokens() tokens
+ * (a whole number of blocks). The workspace holds fp32 partials (m, l,
+ * acc[head_dim]) for every (sequence, head, partition):
+ * pa_decode_workspace_bytes() bytes, or 0 when max_context_len fits one
+ * partition (then no workspace is needed). Both are pure functions of their
+ * arguments; pa_decode_workspace_bytes returns 0 for non-positive sizes.
  */
 int32_t pa_decode_partition_tokens(void);
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                  int32_t max_context_len);
 
 /*
- * paged_attention_decode -- one query per sequence attends to all of its
+ * paged_attention_decode -- one step of autoregressive decoding: the new
+ * token of each sequence attends to the K/V cached for every earlier token
+ * (devpress page, "PagedAttention 是如何工作的": decoding reuses the cached
+ * Key/Value vectors), read from blocks scattered through the pool by
+ * following the sequence's page table (devpress page, "分页式KV缓存"; betteryeah
+ * page, section 2.4, attention across pages; section 2.1, L x d values per
+ * head and sequence). The pages do not write the attention formula; the
+ * reading used is scaled dot-product softmax attention over all of its
  * context_lens[s] cached tokens (the current token included: it is written by
  * pa_reshape_and_cache first):
  *   out[s][h] = softmax_t(scale * <q[s][h], K_t>) . V_t,  t < context_lens[s]
- * with K_t, V_t read through block_tables[s] (scaled dot-product attention is
- * the reading of "attention" used here; the pages do not write the formula).
+ * with K_t, V_t read through block_tables[s].
  *   q           [num_seqs][num_heads][head_dim], dtype
  *   out         [num_seqs][num_heads][head_dim], out_dtype
  *   workspace   NULL disables split-K (one partition per sequence); otherwise
@@ -197,9 +236,14 @@ pa_status pa_paged_attention_decode(void* out, pa_dtype out_dtype, const void* q
 
 /*
  * The two stages of pa_paged_attention_decode, for callers that schedule or
- * time them separately. _partitions takes the same arguments and launches K2
- * only; _reduce then merges the partials of rows with more than one
- * partition. Together they equal pa_paged_attention_decode bit for bit.
+ * time them separately (the split-K design described above; not from the
+ * pages). _partitions takes the same arguments and launches K2 only; _reduce
+ * then merges the partials of rows with more than one partition, with
+ * log-sum-exp weights: M = max_p m_p, out = sum_p acc_p 2^(m_p - M) /
+ * sum_p l_p 2^(m_p - M). Together they equal pa_paged_attention_decode bit
+ * for bit. _reduce needs the same workspace, context_lens and
+ * max_context_len as the _partitions call it follows; it returns PA_OK
+ * without launching when nothing was split (no workspace, or one partition).
  */
 pa_status pa_paged_attention_decode_partitions(void* out, pa_dtype out_dtype, const void* q,
                                                const void* k_cache, const void* v_cache,
@@ -253,7 +297,14 @@ pa_status pa_paged_attention_decode_shared_prefix(
 
 /*
  * paged_attention_prefill -- causal attention of multi-token query chunks
- * over the paged cache. Sequence s owns query rows query_start_loc[s] ..
+ * over the paged cache. The pages let one sequence run in segments across
+ * several batches under a per-step token budget (devpress page, continuous
+ * batching workflow, step 4, and the max_num_batched_tokens setting), so a
+ * prompt is processed as chunks of consecutive tokens, each attending
+ * causally to everything cached before it; attention follows the page table
+ * as in decode (devpress page, "分页式KV缓存"; betteryeah page, section 2.4).
+ * Neither the chunk layout nor the causal alignment is written on the pages;
+ * the reading used is the standard one below. Sequence s owns query rows query_start_loc[s] ..
  * query_start_loc[s+1]-1 (L_s >= 0 of them); its context context_lens[s]
  * INCLUDES the chunk, whose K/V are already cached, so the chunk is the last
  * L_s tokens: row query_start_loc[s] + j sits at position ctx - L_s + j and
