@@ -281,8 +281,12 @@ pa_status pa_paged_attention_decode_reduce(void* out, pa_dtype out_dtype, const 
  *                 16-byte aligned (fp32 partials of the shared and private
  *                 partitions)
  * Other arguments and layouts as for pa_paged_attention_decode. f32 caches
- * run the ordinary decode (same result). A prefix longer than a member's
- * context is clamped on the device (no read past that member's blocks).
+ * run the ordinary decode (same result). A prefix longer than some member's
+ * context breaks the precondition; the device then clamps the group's
+ * prefix to its shortest member's context for every member alike, so reads
+ * stay inside the members' blocks and each output row has one writer (the
+ * result is then that of the shorter prefix, still the members' attention
+ * as long as the clamped prefix's blocks are shared).
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
  */
 size_t pa_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,

@@ -316,17 +316,45 @@ def make_decode_shared_workspace(num_seqs, num_heads, head_dim, max_context_len,
     return torch.empty(max(1, n // 4), dtype=torch.float32, device=device)
 
 
+def check_shared_prefix_groups(block_tables, context_lens, group_starts, prefix_lens, block_size: int):
+    """The shared-prefix call's data preconditions, checked on host copies
+    (this reads device memory, so it synchronises: for tests and debugging,
+    not the serving path). Raises ValueError naming the first broken one."""
+    gs = group_starts.cpu().numpy()
+    pl = prefix_lens.cpu().numpy()
+    ctx = context_lens.cpu().numpy()
+    bt = block_tables.cpu().numpy()
+    S = ctx.shape[0]
+    if gs[0] != 0 or gs[-1] != S or (gs[1:] < gs[:-1]).any():
+        raise ValueError("group_starts must rise from 0 to num_seqs")
+    for g in range(pl.shape[0]):
+        rows = slice(int(gs[g]), int(gs[g + 1]))
+        p = int(pl[g])
+        if p < 0 or p % block_size:
+            raise ValueError(f"prefix_lens[{g}] = {p} is not a non-negative multiple of block_size")
+        if gs[g + 1] > gs[g]:
+            if p > int(ctx[rows].min()):
+                raise ValueError(f"prefix_lens[{g}] = {p} exceeds a member's context length")
+            nb = p // block_size
+            if nb and (bt[rows, :nb] != bt[int(gs[g]), :nb]).any():
+                raise ValueError(f"group {g}'s members do not share the prefix's blocks")
+
+
 def paged_attention_decode_shared_prefix(out, q, k_cache, v_cache, block_tables, context_lens, group_starts,
                                          prefix_lens, scale: float, max_context_len: int, max_group_size: int,
-                                         max_prefix_len: int, workspace):
+                                         max_prefix_len: int, workspace, validate: bool = False):
     """Decode where the rows ``group_starts[g]:group_starts[g+1]`` share their
     first ``prefix_lens[g]`` tokens through aliased blocks; each shared tile is
-    read once per group. Same result as ``paged_attention_decode``."""
+    read once per group. Same result as ``paged_attention_decode``.
+    ``validate=True`` first checks the groups' data preconditions on the host
+    (``check_shared_prefix_groups``; synchronises)."""
     _dev(group_starts, prefix_lens)
     _i32(group_starts, prefix_lens)
     G = int(prefix_lens.shape[0])
     if group_starts.shape != (G + 1,):
         raise ValueError("group_starts must be [num_groups + 1]")
+    if validate:
+        check_shared_prefix_groups(block_tables, context_lens, group_starts, prefix_lens, int(k_cache.shape[2]))
     args = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, workspace)
     # (out, odt, q, kc, vc, bt, ctx, S, H, KVH, D, bs, nb, maxb, maxctx, scale, dt, ws, wsb, stream)
     _check("paged_attention_decode_shared_prefix", lib().pa_paged_attention_decode_shared_prefix(

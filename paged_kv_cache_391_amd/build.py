@@ -35,21 +35,6 @@ def build(out: str = LIB, defines=(), verbose: bool = False) -> str:
     return out
 
 
-def build_probe(verbose: bool = False) -> str:
-    """The standalone HBM read-bandwidth probe (a measurement tool)."""
-    src = os.path.join(HERE, "probes", "hbm_read_probe.hip")
-    out = os.path.join(HERE, "probes", "hbm_read_probe")
-    cmd = ["hipcc", "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", "-o", out, src]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True, stderr=None if verbose else subprocess.PIPE)
-    return out
-
-
 if __name__ == "__main__":
-    if "--probe" in sys.argv:
-        build_probe(verbose=True)
-    else:
-        build(verbose=True)
+    build(verbose=True)
     sys.exit(0)

@@ -30,9 +30,7 @@ pa_status check_cache_shape(int32_t num_heads, int32_t head_dim, int32_t block_s
   return PA_OK;
 }
 
-int64_t max_parts_for(int32_t max_context_len) {
-  return max_context_len <= 0 ? 1 : ceil_div(max_context_len, pa::kPartitionTokens);
-}
+int64_t max_parts_for(int32_t max_context_len) { return pa::partitions_for(max_context_len, pa::kPartitionTokens); }
 
 // Compute units of the current device (0 if it cannot be read: the caller
 // then keeps its default, and the launch reports the device error). The
@@ -101,10 +99,12 @@ pa_status prepare_decode(DecodeCall& call, void* out, pa_dtype out_dtype, const 
   a.num_seqs = num_seqs;
   a.H = num_heads;
   a.max_blocks = max_blocks_per_seq;
+  a.max_ctx = max_context_len;
+  a.num_blocks = num_blocks;
   a.max_parts = (int)grid_parts;
   a.ws_parts = (int)grid_parts;
   // without split-K one partition spans the longest context
-  a.part_tiles = split ? pa::kPartitionTokens / 16 : (int)std::max<int64_t>(1, ceil_div(max_context_len, 16));
+  a.part_tiles = split ? pa::kPartitionTokens / 16 : pa::single_partition_tiles(max_context_len);
   a.scale_log2 = scale * 1.4426950408889634f;
   a.out_f32 = out_dtype == PA_F32 ? 1 : 0;
   call.dt = static_cast<Dt>(dtype);
@@ -174,7 +174,7 @@ pa_status pa_gather_kv(void* k_out, void* v_out, const void* k_cache, const void
     return PA_ERR_INVALID_ARG;
   return hip_status(pa::launch_gather_kv(k_out, v_out, k_cache, v_cache, block_tables, context_lens,
                                          cu_context_lens, num_seqs, max_context_len, num_heads, head_dim,
-                                         block_size, max_blocks_per_seq, elt_bytes(dtype), stream));
+                                         block_size, max_blocks_per_seq, num_blocks, elt_bytes(dtype), stream));
 }
 
 int32_t pa_decode_partition_tokens(void) { return pa::kPartitionTokens; }
@@ -222,6 +222,8 @@ pa_status pa_paged_attention_decode_reduce(void* out, pa_dtype out_dtype, const 
   a.num_rows = num_seqs;
   a.num_seqs = num_seqs;
   a.H = num_heads;
+  a.max_ctx = max_context_len;
+  a.num_blocks = 1;  // reads no blocks
   a.max_parts = (int)parts;
   a.ws_parts = (int)parts;
   a.part_tiles = pa::kPartitionTokens / 16;
@@ -292,6 +294,8 @@ pa_status pa_paged_attention_decode_shared_prefix(
   a.num_seqs = num_seqs;
   a.H = num_heads;
   a.max_blocks = max_blocks_per_seq;
+  a.max_ctx = max_context_len;
+  a.num_blocks = num_blocks;
   a.ws_parts = (int)parts + 1;
   a.part_tiles = pa::kPartitionTokens / 16;
   a.shared_part_tiles = pa::shared_partition_tokens(block_size) / 16;
@@ -370,6 +374,7 @@ static pa_status prepare_prefill(PrefillCall& call, void* out, pa_dtype out_dtyp
     a.H = num_heads;
     a.max_blocks = max_blocks_per_seq;
     a.max_context_len = max_context_len;
+    a.num_blocks = num_blocks;
     a.q_tiles = (int)ceil_div(max_q_len, pa::prefill_mfma_q_tile());
     // a negative scale runs as |scale| on negated queries (a sign flip, exact)
     a.scale_log2 = std::fabs(scale) * 1.4426950408889634f;
@@ -397,9 +402,11 @@ static pa_status prepare_prefill(PrefillCall& call, void* out, pa_dtype out_dtyp
   a.num_seqs = num_seqs;
   a.H = num_heads;
   a.max_blocks = max_blocks_per_seq;
+  a.max_ctx = max_context_len;
+  a.num_blocks = num_blocks;
   a.max_parts = 1;
   a.ws_parts = 1;
-  a.part_tiles = (int)std::max<int64_t>(1, ceil_div(max_context_len, 16));
+  a.part_tiles = pa::single_partition_tiles(max_context_len);
   a.scale_log2 = scale_log2;
   a.out_f32 = 1;
   return PA_OK;

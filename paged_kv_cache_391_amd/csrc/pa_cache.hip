@@ -75,16 +75,16 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(
     uint4* __restrict__ k_out, uint4* __restrict__ v_out, const uint4* __restrict__ k_cache,
     const uint4* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ cu_ctx, int H, int BS, int CPR,
-    int max_blocks) {
+    int max_blocks, int max_ctx, int num_blocks) {
   const int s = blockIdx.y;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // within the sequence
-  const int ctx = context_lens[s];
+  const int ctx = clamp_len(context_lens[s], max_ctx);
   if (i >= (int64_t)ctx * H * CPR) return;
   const int c = (int)(i % CPR);
   const int64_t th = i / CPR;
   const int h = (int)(th % H);
   const int t = (int)(th / H);
-  const int32_t phys = block_tables[(int64_t)s * max_blocks + t / BS];
+  const int32_t phys = clamp_block(block_tables[(int64_t)s * max_blocks + t / BS], num_blocks);
   const int64_t src = kv_row_offset(phys, h, t % BS, H, BS, CPR);  // in 16-byte units
   const int64_t dst = (((int64_t)cu_ctx[s] + t) * H + h) * CPR + c;
   k_out[dst] = k_cache[src + c];
@@ -117,15 +117,15 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block
 
 hipError_t launch_gather_kv(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
                             const int32_t* block_tables, const int32_t* context_lens, const int32_t* cu_ctx,
-                            int S, int max_ctx, int H, int D, int BS, int max_blocks, int elt_bytes,
-                            hipStream_t stream) {
+                            int S, int max_ctx, int H, int D, int BS, int max_blocks, int num_blocks,
+                            int elt_bytes, hipStream_t stream) {
   const int CPR = D * elt_bytes / 16;
   const int64_t per_seq = (int64_t)max_ctx * H * CPR;
   if (per_seq == 0 || S == 0) return hipSuccess;
   const int64_t gx = (per_seq + 255) / 256;
   hipLaunchKernelGGL(gather_kv_kernel, dim3((unsigned)gx, (unsigned)S), dim3(256), 0, stream, (uint4*)k_out,
                      (uint4*)v_out, (const uint4*)k_cache, (const uint4*)v_cache, block_tables, context_lens,
-                     cu_ctx, H, BS, CPR, max_blocks);
+                     cu_ctx, H, BS, CPR, max_blocks, max_ctx, num_blocks);
   return hipGetLastError();
 }
 

@@ -63,7 +63,7 @@ __global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_kernel(const 
   const int row = blockIdx.x / hg;
   const int h = (blockIdx.x % hg) * NW + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (h >= a.H) return;
-  const int ctx = a.context_lens[row];
+  const int ctx = row_ctx(a, row);
   const int nparts = row_parts<MODE>(a, row, ctx).total();
   if (nparts <= 1) return;
   const int lane = threadIdx.x & 63;

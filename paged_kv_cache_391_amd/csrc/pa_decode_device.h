@@ -139,18 +139,21 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float x, int o
   }
 }
 
+// Context length of row r (decode and shared-tail modes), clamped.
+__device__ __forceinline__ int row_ctx(const DecodeArgs& a, int r) { return clamp_len(a.context_lens[r], a.max_ctx); }
+
 // Row r of the prefill-row mode is query j of chunk s: its causal context is
-// ctx[s] - L_s + j + 1 tokens of sequence s.
-__device__ __forceinline__ void prefill_row(const int32_t* qsl, const int32_t* ctx_lens, int S, int r, int& seq,
-                                            int& ctx) {
-  int lo = 0, hi = S - 1;
+// ctx[s] - L_s + j + 1 tokens of sequence s (clamped like any length).
+__device__ __forceinline__ void prefill_row(const DecodeArgs& a, int r, int& seq, int& ctx) {
+  const int32_t* qsl = a.query_start_loc;
+  int lo = 0, hi = a.num_seqs - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (qsl[mid] <= r) lo = mid; else hi = mid - 1;
   }
   seq = lo;
   const int L = qsl[lo + 1] - qsl[lo];
-  ctx = ctx_lens[lo] - L + (r - qsl[lo]) + 1;
+  ctx = clamp_len(a.context_lens[lo] - L + (r - qsl[lo]) + 1, a.max_ctx);
 }
 
 // Group g of a prefix-sharing batch is rows group_starts[g] .. group_starts[g+1]-1.
@@ -170,6 +173,23 @@ __device__ __forceinline__ int group_of_row(const int32_t* group_starts, int num
   return cnt;
 }
 
+// Shared tokens of group g, the same value in every kernel that walks the
+// group: prefix_lens[g], clamped to the shortest member's context (a longer
+// prefix breaks the call's precondition; with the clamp every member still
+// owns the shared range, reads stay inside the members' blocks and the
+// kernels agree on which partitions exist), rounded down to whole 16-token
+// tiles. Called by whole waves (every lane active).
+__device__ __forceinline__ int group_prefix(const DecodeArgs& a, int g) {
+  const int lane = __lane_id();
+  const int r0 = min(max(a.group_starts[g], 0), a.num_rows);
+  const int r1 = min(max(a.group_starts[g + 1], r0), a.num_rows);
+  int p = a.prefix_lens[g];
+  for (int r = r0 + lane; r < r1; r += 64) p = min(p, row_ctx(a, r));
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) p = min(p, __shfl_xor(p, s));
+  return max(p, 0) & ~15;
+}
+
 // Partition layout of one row: own partitions cover tokens [tok0, ctx) in
 // part_tiles-tile steps and sit in workspace slots poff, poff+1, ...; a row
 // of a prefix-sharing group has ceil(prefix / shared partition) shared
@@ -182,15 +202,12 @@ template <RowMode MODE>
 __device__ __forceinline__ RowParts row_parts(const DecodeArgs& a, int row, int ctx) {
   RowParts rp{0, 0, 0};
   if constexpr (MODE == RowMode::SharedTail) {
-    // the prefix is whole tiles inside the row (clamped so that a prefix
-    // longer than the row can never send a read past the row's blocks)
-    const int p = min(a.prefix_lens[group_of_row(a.group_starts, a.num_groups, row)], ctx) & ~15;
+    const int p = group_prefix(a, group_of_row(a.group_starts, a.num_groups, row));
     const int pt = a.shared_part_tiles * 16;
     rp.tok0 = p;
     rp.poff = (p + pt - 1) / pt;
   }
-  const int own_tiles = ((ctx + 15) >> 4) - (rp.tok0 >> 4);
-  rp.own = (own_tiles + a.part_tiles - 1) / a.part_tiles;
+  rp.own = own_partitions(ctx, rp.tok0, a.part_tiles);
   return rp;
 }
 
@@ -221,10 +238,10 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int b
 
   int seq, ctx;
   if constexpr (MODE == RowMode::PrefillRows) {
-    prefill_row(a.query_start_loc, a.context_lens, a.num_seqs, row, seq, ctx);
+    prefill_row(a, row, seq, ctx);
   } else {
     seq = row;
-    ctx = a.context_lens[row];
+    ctx = row_ctx(a, row);
   }
   const int n_tiles = (ctx + 15) >> 4;
   const RowParts rp = row_parts<MODE>(a, row, ctx);
@@ -259,10 +276,10 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int b
     if (lane < cnt) {
       const int u = u0 + base + lane;
       if constexpr (BS >= 16) {
-        tb = bt_row[u / TPB];
+        tb = clamp_block(bt_row[u / TPB], a.num_blocks);
       } else {
-        tb = bt_row[2 * u];
-        tb2 = 2 * u + 1 < (ctx + 7) / 8 ? bt_row[2 * u + 1] : tb;
+        tb = clamp_block(bt_row[2 * u], a.num_blocks);
+        tb2 = 2 * u + 1 < (ctx + 7) / 8 ? clamp_block(bt_row[2 * u + 1], a.num_blocks) : tb;
       }
     }
 

@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pa_bounds.h"
+
 namespace pa {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));

@@ -67,6 +67,8 @@ struct DecodeArgs {
   int num_seqs;
   int H;
   int max_blocks;
+  int max_ctx;                      // the call's max_context_len: contexts are clamped to it
+  int num_blocks;                   // pool size: block ids are clamped below it
   int max_parts;                    // partitions per row in the grid
   int ws_parts;                     // partition slots per (row, head) in the workspace
   int part_tiles;                   // 16-token tiles per partition
@@ -86,8 +88,8 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block
                               int D, int BS, int num_blocks, int elt_bytes, hipStream_t stream);
 hipError_t launch_gather_kv(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
                             const int32_t* block_tables, const int32_t* context_lens, const int32_t* cu_ctx,
-                            int S, int max_ctx, int H, int D, int BS, int max_blocks, int elt_bytes,
-                            hipStream_t stream);
+                            int S, int max_ctx, int H, int D, int BS, int max_blocks, int num_blocks,
+                            int elt_bytes, hipStream_t stream);
 
 // partition kernel (K2) over the rows `mode` describes
 hipError_t launch_decode_partitions(const DecodeArgs& a, Dt dt, int D, int BS, RowMode mode, hipStream_t stream);
@@ -115,6 +117,7 @@ struct PrefillArgs {
   int H;
   int max_blocks;
   int max_context_len;
+  int num_blocks;
   int q_tiles;                      // grid: q tiles per sequence
   int grouped;                      // grid order: query tiles of a (sequence, head) pair together
   float scale_log2;                 // |scale| * log2(e)

@@ -188,11 +188,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
     bid /= a.num_seqs;
     qt = a.q_tiles - 1 - bid;
   }
-  const int q_beg = a.query_start_loc[s];
-  const int L = a.query_start_loc[s + 1] - q_beg;
+  // lengths and row ranges clamped to what the host validated (in-range
+  // values are unchanged): no read or write leaves the caller's buffers
+  const ChunkRows cr =
+      chunk_rows(a.query_start_loc[s], a.query_start_loc[s + 1], a.context_lens[s], a.total_q, a.max_context_len);
+  const int ctx = cr.ctx, q_beg = cr.q_beg, L = cr.L;
   const int j0 = qt * QT;
   if (j0 >= L) return;
-  const int ctx = a.context_lens[s];
   const int c0 = ctx - L;                          // position of the chunk's first query
   const int kv_end = c0 + min(j0 + QT, L);         // keys this workgroup needs: [0, kv_end)
   const int n_tiles = (kv_end + KT - 1) / KT;
@@ -261,7 +263,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
     for (int i = 0; i < PPW; ++i) {
       const int p = wave + 4 * i;
       const uint32_t key = (uint32_t)(t * KT + p * PR);
-      const uint64_t row = (uint64_t)(uint32_t)phys[i] * blk_bytes + (head_bytes + (key % BS) * ROWB);
+      const uint64_t row =
+          (uint64_t)(uint32_t)clamp_block(phys[i], a.num_blocks) * blk_bytes + (head_bytes + (key % BS) * ROWB);
       lds_dma16s(kc + row, k_src, sk0 + b * TILEB + p * 1024);
       lds_dma16s(vc + row, v_src, sv0 + b * TILEB + p * 1024);
     }

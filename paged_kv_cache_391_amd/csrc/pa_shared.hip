@@ -53,12 +53,12 @@ __device__ __forceinline__ void shared_prefix_body(const DecodeArgs& a, int bid)
   const int grp = bid % a.num_groups;
   const int part = bid / a.num_groups;
 
-  const int r_begin = a.group_starts[grp];
+  const int r_begin = min(max(a.group_starts[grp], 0), a.num_rows);
   const int m0 = r_begin + 16 * mc;
-  const int nm = min(16, a.group_starts[grp + 1] - m0);
+  const int nm = min(16, min(max(a.group_starts[grp + 1], r_begin), a.num_rows) - m0);
   if (nm <= 0) return;
   const int pt = a.shared_part_tiles * 16;
-  const int prefix = min(a.prefix_lens[grp], a.context_lens[r_begin]) & ~15;  // whole tiles of the first member
+  const int prefix = group_prefix(a, grp);  // whole tiles every member holds
   const int ns = (prefix + pt - 1) / pt;
   if (part >= ns) return;
   const int k_begin = part * pt;
@@ -78,7 +78,7 @@ __device__ __forceinline__ void shared_prefix_body(const DecodeArgs& a, int bid)
   // table entries of the partition's blocks (at most 64), read out with readlane
   const int32_t* bt_row = a.block_tables + (int64_t)r_begin * a.max_blocks + k_begin / BS;
   const int nblk = (k_end - k_begin + BS - 1) / BS;
-  const int32_t tb = lane < nblk ? bt_row[lane] : 0;
+  const int32_t tb = lane < nblk ? clamp_block(bt_row[lane], a.num_blocks) : 0;
   const char* kc = reinterpret_cast<const char*>(a.k_cache);
   const char* vc = reinterpret_cast<const char*>(a.v_cache);
   // byte offset of partition-relative key `key` (wave-uniform); a 16-key
@@ -231,9 +231,8 @@ __device__ __forceinline__ void shared_prefix_body(const DecodeArgs& a, int bid)
   const float lt = rows4_sum(l);
   if (n16 >= nm) return;
   const int row = m0 + n16;
-  const int ctx = a.context_lens[row];
-  const int own_tiles = ((ctx + 15) >> 4) - (prefix >> 4);
-  const int total = ns + (own_tiles + a.part_tiles - 1) / a.part_tiles;
+  const int ctx = row_ctx(a, row);
+  const int total = ns + own_partitions(ctx, prefix, a.part_tiles);
   if (total <= 1) {
     const int64_t orow = ((int64_t)row * a.H + h) * D;
 #pragma unroll

@@ -170,3 +170,23 @@ def test_attention_step_validation():
     a.num_new_tokens = 0
     a.num_decode_seqs, a.decode_max_blocks_per_seq, a.decode_max_context_len = 2, 4, 100  # q/out missing
     assert L.pa_attention_step(ctypes.byref(a), NULL, NULL, NULL, NULL) == pa.PA_ERR_INVALID_ARG
+
+
+def test_shared_prefix_group_check_rejects_broken_groups():
+    """The binding's host-side check of the shared-prefix preconditions
+    (CPU tensors, no launch)."""
+    import torch
+    bt = torch.tensor([[3, 4, 5], [3, 4, 6], [7, 8, 9]], dtype=torch.int32)
+    ctx = torch.tensor([40, 33, 20], dtype=torch.int32)
+    gs = torch.tensor([0, 2, 3], dtype=torch.int32)
+    ok = torch.tensor([32, 16], dtype=torch.int32)
+    pa.check_shared_prefix_groups(bt, ctx, gs, ok, 16)
+    bad = {"exceeds": ([48, 16], [0, 2, 3]), "multiple": ([24, 16], [0, 2, 3]), "rise": ([32, 16], [0, 3, 2])}
+    for why, (pl, starts) in bad.items():
+        with pytest.raises(ValueError, match=why):
+            pa.check_shared_prefix_groups(bt, ctx, torch.tensor(starts, dtype=torch.int32),
+                                          torch.tensor(pl, dtype=torch.int32), 16)
+    bt2 = bt.clone()
+    bt2[1, 1] = 99  # second shared block differs
+    with pytest.raises(ValueError, match="share"):
+        pa.check_shared_prefix_groups(bt2, ctx, gs, ok, 16)

@@ -30,3 +30,15 @@ def test_c_program_matches_the_oracle_and_the_step_call():
     assert vals["step_bit_identical"] == "1"
     assert float(vals["step_max_abs_err"]) <= 2e-3
     assert float(vals["step_prefill_max_abs_err"]) <= 2e-3
+
+
+def test_kernel_index_arithmetic_stays_in_bounds():
+    """Lengths, block ids and query ranges far outside the preconditions
+    (negative, past max_context_len, past the pool, INT_MIN/INT_MAX) are
+    clamped by the functions every kernel and launch plan uses, so no table
+    entry, workspace slot, query row or block outside the validated sizes is
+    touched. Host code only (tests/c_abi/bounds_check.cpp)."""
+    exe = c_abi_build.build_bounds()
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.startswith("bounds ok")

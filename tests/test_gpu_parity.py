@@ -415,7 +415,7 @@ def _shared_decode(od, wl, gs, pl, max_group, out_dtype=torch.float32):
     ws = pa.make_decode_shared_workspace(d.num_seqs, wl.num_heads, wl.head_dim, d.max_context_len)
     pa.paged_attention_decode_shared_prefix(out, od.q, od.k_cache, od.v_cache, od.block_tables, od.context_lens,
                                             dev(gs), dev(pl), wl.scale, d.max_context_len, max_group,
-                                            int(pl.max()), ws)
+                                            int(pl.max()), ws, validate=True)
     return out
 
 
@@ -488,7 +488,7 @@ def test_shared_prefix_decode_ragged_groups(dtype, bs):
     ws = pa.make_decode_shared_workspace(len(ctx), H, D, maxctx)
     dq, dk, dv = dev(q, dtype), dev(kc, dtype), dev(vc, dtype)
     pa.paged_attention_decode_shared_prefix(out, dq, dk, dv, dev(bt), dev(ctx), dev(gs), dev(pl), scale, maxctx,
-                                            int(np.diff(gs).max()), int(pl.max()), ws)
+                                            int(np.diff(gs).max()), int(pl.max()), ws, validate=True)
     _check_attention(out, ref, dtype)
     again = torch.empty_like(out)
     pa.paged_attention_decode_shared_prefix(again, dq, dk, dv, dev(bt), dev(ctx), dev(gs), dev(pl), scale, maxctx,
@@ -512,7 +512,8 @@ def test_shared_prefix_decode_more_groups_than_a_wave_has_lanes():
     maxctx = int(ctx.max())
     ws = pa.make_decode_shared_workspace(len(ctx), H, D, maxctx)
     pa.paged_attention_decode_shared_prefix(out, dev(q, "f16"), dev(kc, "f16"), dev(vc, "f16"), dev(bt), dev(ctx),
-                                            dev(gs), dev(pl), scale, maxctx, int(np.diff(gs).max()), int(pl.max()), ws)
+                                            dev(gs), dev(pl), scale, maxctx, int(np.diff(gs).max()), int(pl.max()), ws,
+                                            validate=True)
     _check_attention(out, ref, "f16")
 
 
