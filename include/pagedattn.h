@@ -54,7 +54,8 @@ typedef enum {
   PA_ERR_HIP = -4,         /* a launch failed; hipGetLastError() was cleared */
   PA_ERR_NO_BLOCKS = -5,   /* block allocator: not enough free blocks (nothing was changed) */
   PA_ERR_NO_MEMORY = -6,   /* block allocator: host memory allocation failed */
-  PA_ERR_PENDING_WRITES = -7 /* block allocator: the copy source still has writes in the open batch */
+  PA_ERR_PENDING_WRITES = -7, /* block allocator: the copy source still has writes in the open batch */
+  PA_ERR_SCRATCH_LIMIT = -8   /* allocation-free decode: the request needs more than its built-in scratch */
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
@@ -233,6 +234,32 @@ pa_status pa_paged_attention_decode(void* out, pa_dtype out_dtype, const void* q
                                     int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                                     float scale, pa_dtype dtype, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
+
+/*
+ * paged_attention_decode_noalloc -- pa_paged_attention_decode with split-K
+ * always on and no workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). The split-K partials live in a scratch
+ * array built into the library: pa_decode_noalloc_scratch_bytes() bytes
+ * (64 MiB) per device, held from the library's load until the process ends.
+ * The call allocates nothing and gives the same result, bit for bit, as
+ * pa_paged_attention_decode with a workspace. Every call on a device shares
+ * that device's array: calls that may overlap on one device (different
+ * streams with no ordering between them) race and must not be issued.
+ * Arguments as for pa_paged_attention_decode, without workspace and
+ * workspace_bytes. Errors: those of pa_paged_attention_decode except
+ * WORKSPACE, and SCRATCH_LIMIT when pa_decode_workspace_bytes(num_seqs,
+ * num_heads, head_dim, max_context_len) exceeds the scratch (nothing is
+ * launched); HIP if the scratch's device address cannot be obtained.
+ */
+size_t pa_decode_noalloc_scratch_bytes(void);
+pa_status pa_paged_attention_decode_noalloc(void* out, pa_dtype out_dtype, const void* q, const void* k_cache,
+                                            const void* v_cache, const int32_t* block_tables,
+                                            const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                            int32_t num_blocks, int32_t max_blocks_per_seq,
+                                            int32_t max_context_len, float scale, pa_dtype dtype,
+                                            hipStream_t stream);
 
 /*
  * The two stages of pa_paged_attention_decode, for callers that schedule or

@@ -30,7 +30,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = 0, -1, -2, -3, -4
-PA_ERR_NO_BLOCKS, PA_ERR_NO_MEMORY, PA_ERR_PENDING_WRITES = -5, -6, -7
+PA_ERR_NO_BLOCKS, PA_ERR_NO_MEMORY, PA_ERR_PENDING_WRITES, PA_ERR_SCRATCH_LIMIT = -5, -6, -7, -8
 _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 _lib = None
 
@@ -78,6 +78,10 @@ def lib():
         dec = [P, ctypes.c_int, P, P, P, P, P, I, I, I, I, I, I, I, I, F, ctypes.c_int, P, Z, P]
         L.pa_paged_attention_decode.argtypes = dec
         L.pa_paged_attention_decode_partitions.argtypes = dec
+        L.pa_paged_attention_decode_noalloc.argtypes = dec[:17] + [P]
+        L.pa_paged_attention_decode_noalloc.restype = ctypes.c_int
+        L.pa_decode_noalloc_scratch_bytes.argtypes = []
+        L.pa_decode_noalloc_scratch_bytes.restype = Z
         L.pa_paged_attention_decode_reduce.argtypes = [P, ctypes.c_int, P, I, I, I, I, ctypes.c_int, P, Z, P]
         L.pa_paged_attention_prefill.argtypes = [P, ctypes.c_int, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F,
                                                  ctypes.c_int, P]
@@ -305,6 +309,20 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     split-K over long contexts. Pass ``max_context_len`` to avoid a sync."""
     _check("paged_attention_decode", lib().pa_paged_attention_decode(
         *_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, workspace)))
+
+
+def decode_noalloc_scratch_bytes() -> int:
+    """Size of the split-K scratch built into the library (per device)."""
+    return int(lib().pa_decode_noalloc_scratch_bytes())
+
+
+def paged_attention_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                                   max_context_len: int | None = None):
+    """``paged_attention_decode`` with split-K on and its partials in the
+    library's built-in scratch: the call allocates nothing. Calls that may
+    overlap on one device race (they share the scratch)."""
+    args = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, None)
+    _check("paged_attention_decode_noalloc", lib().pa_paged_attention_decode_noalloc(*args[:17], args[19]))
 
 
 def decode_shared_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int) -> int:

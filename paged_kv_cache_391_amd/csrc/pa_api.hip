@@ -57,6 +57,40 @@ int device_compute_units() {
   return cus;
 }
 
+// Split-K scratch of pa_paged_attention_decode_noalloc: a file-scope device
+// array, so that call allocates nothing. Every device the library runs on
+// holds its own copy from module load until the process ends. In host code
+// the array's name is not a device address: its device address comes from
+// hipGetSymbolAddress, fetched once per device (scratch_on_device) and used
+// wherever host code hands the memory to a kernel. All calls on a device
+// share its copy; the partials it holds are written before they are read
+// within one call, so nothing in it needs to start at zero, and calls that
+// overlap on one device (different streams, no ordering) race.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+// Device address of this device's scratch (nullptr if the runtime cannot
+// give it; the call then reports PA_ERR_HIP).
+float* scratch_on_device() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<float*> known[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  float* p = known[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* sym = nullptr;
+  if (hipGetSymbolAddress(&sym, HIP_SYMBOL(scratch)) != hipSuccess || !sym) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  p = static_cast<float*>(sym);
+  known[dev].store(p, std::memory_order_release);  // racing first calls store the same address
+  return p;
+}
+
 struct DecodeCall {
   pa::DecodeArgs args;
   Dt dt;
@@ -128,6 +162,7 @@ const char* pa_status_string(pa_status status) {
     case PA_ERR_NO_BLOCKS: return "no free KV block left in the pool";
     case PA_ERR_NO_MEMORY: return "host memory allocation failed";
     case PA_ERR_PENDING_WRITES: return "copy source still has writes in the open batch: take_copies first";
+    case PA_ERR_SCRATCH_LIMIT: return "request needs more split-K scratch than the allocation-free call holds (64 MiB)";
   }
   return "unknown status";
 }
@@ -242,6 +277,33 @@ pa_status pa_paged_attention_decode(void* out, pa_dtype out_dtype, const void* q
   pa_status st = prepare_decode(call, out, out_dtype, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
                                 num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                                 max_context_len, scale, dtype, workspace, workspace_bytes);
+  if (st != PA_OK || num_seqs == 0) return st;
+  hipError_t e = pa::launch_decode_partitions(call.args, call.dt, call.D, call.BS, pa::RowMode::Decode, stream);
+  if (e == hipSuccess && call.split) e = pa::launch_decode_reduce(call.args, call.dt, call.D, false, stream);
+  return hip_status(e);
+}
+
+size_t pa_decode_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+pa_status pa_paged_attention_decode_noalloc(void* out, pa_dtype out_dtype, const void* q, const void* k_cache,
+                                            const void* v_cache, const int32_t* block_tables,
+                                            const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                            int32_t num_blocks, int32_t max_blocks_per_seq,
+                                            int32_t max_context_len, float scale, pa_dtype dtype,
+                                            hipStream_t stream) {
+  // the scratch a split-K launch of this size needs must fit the built-in array
+  const size_t need = pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len);
+  if (need > kNoAllocScratchBytes) return PA_ERR_SCRATCH_LIMIT;
+  float* ws = nullptr;
+  if (need > 0) {
+    ws = scratch_on_device();
+    if (!ws) return PA_ERR_HIP;
+  }
+  DecodeCall call;
+  pa_status st = prepare_decode(call, out, out_dtype, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                                num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                max_context_len, scale, dtype, ws, need);
   if (st != PA_OK || num_seqs == 0) return st;
   hipError_t e = pa::launch_decode_partitions(call.args, call.dt, call.D, call.BS, pa::RowMode::Decode, stream);
   if (e == hipSuccess && call.split) e = pa::launch_decode_reduce(call.args, call.dt, call.D, false, stream);

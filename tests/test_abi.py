@@ -190,3 +190,17 @@ def test_shared_prefix_group_check_rejects_broken_groups():
     bt2[1, 1] = 99  # second shared block differs
     with pytest.raises(ValueError, match="share"):
         pa.check_shared_prefix_groups(bt2, ctx, gs, ok, 16)
+
+
+def test_noalloc_decode_refuses_past_its_scratch_before_any_launch():
+    """The allocation-free decode checks the scratch its request needs
+    against the built-in size first (fake pointers: nothing is launched)."""
+    L = pa.lib()
+    limit = L.pa_decode_noalloc_scratch_bytes()
+    assert limit == 64 << 20
+    S, H, D = 256, 32, 128
+    ctx = 1 << 20                             # 2048 partitions per row: far past the scratch
+    assert L.pa_decode_workspace_bytes(S, H, D, ctx) > limit
+    rc = L.pa_paged_attention_decode_noalloc(FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE, S, H, H, D, 16, 1 << 16,
+                                             ctx // 16, ctx, 0.1, 1, NULL)
+    assert rc == pa.PA_ERR_SCRATCH_LIMIT
