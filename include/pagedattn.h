@@ -197,7 +197,8 @@ pa_status pa_gather_kv(void* k_out, void* v_out, const void* k_cache, const void
  * acc[head_dim]) for every (sequence, head, partition):
  * pa_decode_workspace_bytes() bytes, or 0 when max_context_len fits one
  * partition (then no workspace is needed). Both are pure functions of their
- * arguments; pa_decode_workspace_bytes returns 0 for non-positive sizes.
+ * arguments; pa_decode_workspace_bytes returns 0 for non-positive sizes and
+ * SIZE_MAX for sizes whose partials would not fit in size_t.
  */
 int32_t pa_decode_partition_tokens(void);
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,

@@ -30,6 +30,16 @@ pa_status check_cache_shape(int32_t num_heads, int32_t head_dim, int32_t block_s
   return PA_OK;
 }
 
+// Bytes of fp32 split-K partials (acc[head_dim], m, l) for rows x heads x
+// slots, all positive; SIZE_MAX when the product does not fit in size_t
+// (no launch of that size can pass validation anyway). The factors are
+// below 2^31 (slots below 2^23), so the product fits 128 bits.
+size_t partial_bytes(int64_t rows, int64_t heads, int64_t slots, int64_t head_dim) {
+  const unsigned __int128 b = (unsigned __int128)rows * (uint64_t)heads * (uint64_t)slots *
+                              (uint64_t)(head_dim + 2) * sizeof(float);
+  return b > (unsigned __int128)SIZE_MAX ? SIZE_MAX : (size_t)b;
+}
+
 int64_t max_parts_for(int32_t max_context_len) { return pa::partitions_for(max_context_len, pa::kPartitionTokens); }
 
 // Compute units of the current device (0 if it cannot be read: the caller
@@ -219,7 +229,7 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t he
   if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
   const int64_t parts = max_parts_for(max_context_len);
   if (parts <= 1) return 0;
-  return (size_t)num_seqs * num_heads * parts * (head_dim + 2) * sizeof(float);
+  return partial_bytes(num_seqs, num_heads, parts, head_dim);
 }
 
 pa_status pa_paged_attention_decode_partitions(void* out, pa_dtype out_dtype, const void* q,
@@ -316,7 +326,7 @@ size_t pa_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int
   // shared + own partitions of one row: ceil(p / shared) + ceil((ctx - p) / own) for a prefix of p
   // tokens, at most ceil(ctx / own) + 1 as shared partitions are no shorter than own ones
   const int64_t slots = max_parts_for(max_context_len) + 1;
-  return (size_t)num_seqs * num_heads * slots * (head_dim + 2) * sizeof(float);
+  return partial_bytes(num_seqs, num_heads, slots, head_dim);
 }
 
 pa_status pa_paged_attention_decode_shared_prefix(
