@@ -456,6 +456,7 @@ static pa_status prepare_prefill(PrefillCall& call, void* out, pa_dtype out_dtyp
     // more workgroups than the chip holds at once: group each pair's query
     // tiles for L2 reuse (the kernel's work-order note)
     const int cus = device_compute_units();
+    a.cus = cus;
     a.grouped = cus > 0 && (int64_t)a.q_tiles * num_heads * num_seqs > (int64_t)cus * pa::kPrefillWorkgroupsPerCU;
     return PA_OK;
   }

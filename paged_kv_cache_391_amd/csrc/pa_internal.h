@@ -120,6 +120,7 @@ struct PrefillArgs {
   int num_blocks;
   int q_tiles;                      // grid: q tiles per sequence
   int grouped;                      // grid order: query tiles of a (sequence, head) pair together
+  int cus;                          // compute units of the device (0: unknown)
   float scale_log2;                 // |scale| * log2(e)
   uint32_t q_sign;                  // 0x80008000 for a negative scale (queries negated), else 0
   int out_f32;

@@ -46,6 +46,7 @@
 #include "pa_internal.h"
 
 #include <type_traits>
+#include <utility>
 
 namespace pa {
 
@@ -58,10 +59,28 @@ namespace {
 #define PA_PREFILL_NQ 2
 #endif
 constexpr int KT = PA_PREFILL_KT;  // keys per tile (32 or 64)
-constexpr int NQ = PA_PREFILL_NQ;  // 16-query groups per wave
-constexpr int QW = 16 * NQ;        // queries per wave
-constexpr int QT = 4 * QW;         // queries per workgroup
-constexpr int NBUF = 3;            // LDS buffers per operand: tile t computed while t+1, t+2 land
+#ifndef PA_PREFILL_NW
+#define PA_PREFILL_NW 4
+#endif
+#ifndef PA_PREFILL_WAVES
+#define PA_PREFILL_WAVES 3
+#endif
+// Shape per head dim: NW waves per workgroup, NQ 16-query groups per wave;
+// every shape covers QT queries per workgroup.
+template <int D> struct PfShape {
+  static constexpr int NW = D == 128 ? PA_PREFILL_NW : 4;
+  static constexpr int NQ = D == 128 ? PA_PREFILL_NQ : 2;
+  static constexpr int QW = 16 * NQ;  // queries per wave
+  static constexpr int QT = NW * QW;  // queries per workgroup
+  static constexpr int WAVES = D == 128 ? PA_PREFILL_WAVES : 3;  // waves per SIMD the registers must allow
+};
+constexpr int QT = PfShape<128>::QT;
+static_assert(PfShape<64>::QT == QT, "one query tile for every head dim");
+#ifndef PA_PREFILL_NBUF
+#define PA_PREFILL_NBUF 3
+#endif
+constexpr int NBUF = PA_PREFILL_NBUF;  // LDS buffers per operand: tile t computed while t+1 .. t+NBUF-1 land
+static_assert(NBUF >= 2, "at least one tile in flight");
 constexpr float RESCALE_LOG2 = 8.f; // lazy rescale threshold (log2 units): p < 256 between rescales
 static_assert(KT == 32, "key tile of 32");
 
@@ -113,19 +132,27 @@ __device__ __forceinline__ void sload2(const int32_t* p0, const int32_t* p1, int
                : "=&s"(v0), "=&s"(v1) : "s"(p0), "s"(p1) : "memory");
 }
 // The top of a pipeline step: the scalar loads of the next DMA's block ids
-// (PPW of them), the wait until at most 2 PPW of this wave's DMA loads are
-// outstanding, the workgroup barrier, then the wait for the scalar loads,
+// (PPW of them), the wait until at most VMCNT of this wave's DMA loads are
+// outstanding (the tiles still in flight behind the one about to be
+// computed), the workgroup barrier, then the wait for the scalar loads,
 // whose latency thus hides behind the barrier.
-template <int PPW>
+template <int PPW, int VMCNT>
 __device__ __forceinline__ void sload_barrier(const int32_t* const (&e)[PPW], int32_t (&v)[PPW]) {
   static_assert(PPW == 1 || PPW == 2, "one or two DMA pieces per wave");
+  static_assert(VMCNT >= 0 && VMCNT <= 63, "vmcnt field");
   if constexpr (PPW == 2)
-    asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt vmcnt(4)\n\ts_barrier\n\t"
+    asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt vmcnt(%4)\n\ts_barrier\n\t"
                  "s_waitcnt lgkmcnt(0)"
-                 : "=&s"(v[0]), "=&s"(v[1]) : "s"(e[0]), "s"(e[1]) : "memory");
+                 : "=&s"(v[0]), "=&s"(v[1]) : "s"(e[0]), "s"(e[1]), "i"(VMCNT) : "memory");
   else
-    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt vmcnt(2)\n\ts_barrier\n\ts_waitcnt lgkmcnt(0)"
-                 : "=&s"(v[0]) : "s"(e[0]) : "memory");
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt vmcnt(%2)\n\ts_barrier\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&s"(v[0]) : "s"(e[0]), "i"(VMCNT) : "memory");
+}
+// f(integral_constant<int, B>) for B = 0, 1, ..., in order (an unrolled loop
+// whose index is a compile-time constant in the body)
+template <typename F, int... B>
+__device__ __forceinline__ void for_each_const(F&& f, std::integer_sequence<int, B...>) {
+  (f(std::integral_constant<int, B>{}), ...);
 }
 template <typename T> __device__ __forceinline__ uint32_t lds_offset(T* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)p;
@@ -134,7 +161,8 @@ template <typename T> __device__ __forceinline__ uint32_t lds_offset(T* p) {
 }  // namespace
 
 template <Dt DT, int D, int BS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void prefill_mfma_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(PfShape<D>::NW * 64) __attribute__((amdgpu_waves_per_eu(PfShape<D>::WAVES))) void prefill_mfma_kernel(const PrefillArgs a) {
+  constexpr int NW = PfShape<D>::NW, NQ = PfShape<D>::NQ, QW = PfShape<D>::QW;
   constexpr int KS = D / 32;     // MFMA k-steps over head_dim for Q.K
   constexpr int NDT = D / 16;    // 16-row tiles of O^T
   constexpr int NSUB = KT / 16;  // 16-key subtiles of S^T
@@ -143,7 +171,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   constexpr int ROWB = D * 2;    // bytes per K/V row
   constexpr int TILEB = KT * ROWB;       // bytes of one K (or V) tile in LDS
   constexpr int PR = 1024 / ROWB;        // rows per 1 KiB DMA piece (one wave-wide load)
-  constexpr int PPW = TILEB / 1024 / 4;  // pieces per wave, per operand and tile
+  constexpr int PPW = TILEB / 1024 / NW;  // pieces per wave, per operand and tile
   static_assert(PR <= BS && BS % PR == 0, "the rows of one DMA piece lie in one block");
   static_assert(PPW >= 1, "every wave loads a piece of each tile");
 
@@ -169,8 +197,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   // query tiles of a pair land on one XCD one after another and walk the
   // same keys together while the K/V tiles sit in that XCD's L2 (each K/V
   // byte then leaves HBM about once instead of once per query tile).
-  // Otherwise every workgroup is resident at once and the latest (heaviest)
-  // query tiles of all pairs go first, each to its own compute unit.
+  // Otherwise every workgroup is resident at once; the (sequence, query
+  // tile) items are then taken heaviest first (priced from the lengths on
+  // the device), and the rounds in which the workgroups reach the compute
+  // units alternate direction, so heavy and light items share units.
   int h, s, qt;
   if (a.grouped) {
     const int x = blockIdx.x & 7;
@@ -181,12 +211,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
     s = pair / a.H;
     qt = a.q_tiles - 1 - rest % a.q_tiles;
   } else {
-    int bid = blockIdx.x;
-    h = bid % a.H;
-    bid /= a.H;
-    s = bid % a.num_seqs;
-    bid /= a.num_seqs;
-    qt = a.q_tiles - 1 - bid;
+    // Workgroups are handed to compute units in order, one per unit per
+    // round (workgroup x, x + CUs, x + 2 CUs, ... share a unit). Every
+    // other round runs backwards, so the unit that holds one of the
+    // heaviest query tiles of the first round gets one of the lightest of
+    // the second.
+    int pos = blockIdx.x;
+    if (a.cus > 0) {
+      const int round = pos / a.cus, c = pos % a.cus;
+      if ((round & 1) && (round + 1) * a.cus <= (int)gridDim.x) pos = round * a.cus + (a.cus - 1 - c);
+    }
+    const int rank = pos / a.H;
+    h = pos % a.H;
+    const int n_items = a.num_seqs * a.q_tiles;
+    if (n_items <= 64) {
+      // Lane i prices work item i (sequence i / q_tiles, query tile
+      // i % q_tiles) at the key tiles its workgroup walks (0 when the chunk
+      // has no such query tile); the grid takes items by decreasing price,
+      // ties in index order, so the heaviest query tiles start first, one
+      // per compute unit. (More items than lanes: the fixed order, latest
+      // query tiles first.)
+      int price = -1;
+      if (lane < n_items) {
+        const int si = lane / a.q_tiles, qi = lane % a.q_tiles;
+        const ChunkRows r = chunk_rows(a.query_start_loc[si], a.query_start_loc[si + 1], a.context_lens[si],
+                                       a.total_q, a.max_context_len);
+        price = qi * QT < r.L ? (r.ctx - r.L + min((qi + 1) * QT, r.L) + KT - 1) / KT : 0;
+      }
+      int ahead = 0;  // items taken before item `lane`
+      for (int j = 0; j < n_items; ++j) {
+        const int pj = __builtin_amdgcn_readlane(price, j);
+        ahead += (pj > price || (pj == price && j < lane)) ? 1 : 0;
+      }
+      const uint64_t hit = __ballot(lane < n_items && ahead == rank);
+      const int item = hit ? (int)__builtin_ctzll(hit) : 0;  // exactly one lane holds each rank
+      s = item / a.q_tiles;
+      qt = item % a.q_tiles;
+    } else {
+      s = rank % a.num_seqs;
+      qt = a.q_tiles - 1 - rank / a.num_seqs;
+    }
   }
   // lengths and row ranges clamped to what the host validated (in-range
   // values are unchanged): no read or write leaves the caller's buffers
@@ -254,14 +318,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   const uint32_t sv0 = lds_offset(&sv[0][0]);
   // block-table entry of piece i of tile t (clamped to the blocks read)
   auto entry = [&](int t, int i) {
-    const uint32_t k = (uint32_t)(t * KT + (wave + 4 * i) * PR);
+    const uint32_t k = (uint32_t)(t * KT + (wave + NW * i) * PR);
     return bt_row + min(k / BS, (uint32_t)(nb - 1));
   };
   // DMA of tile t into buffer b given its pieces' block ids
   auto dma_ids = [&](int t, int b, const int (&phys)[PPW]) {
 #pragma unroll
     for (int i = 0; i < PPW; ++i) {
-      const int p = wave + 4 * i;
+      const int p = wave + NW * i;
       const uint32_t key = (uint32_t)(t * KT + p * PR);
       const uint64_t row =
           (uint64_t)(uint32_t)clamp_block(phys[i], a.num_blocks) * blk_bytes + (head_bytes + (key % BS) * ROWB);
@@ -273,7 +337,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   // weights are zero, but the slots may hold anything, NaN included)
   auto zero_tail = [&](int t, int b) {
     const int r0 = kv_end - t * KT;
-    for (int i = tid; i < (KT - r0) * CPR; i += 256)
+    for (int i = tid; i < (KT - r0) * CPR; i += NW * 64)
       *reinterpret_cast<u32x4*>(&sv[b][(r0 + i / CPR) * ROWB + (i % CPR) * 16]) = u32x4{0u, 0u, 0u, 0u};
   };
   // MFMA operand offsets (bytes inside a buffer): K fragment of k-step ks is
@@ -288,10 +352,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   const uint32_t v_rd = vkey * ROWB + (((n16 & 3) >> 1) * 16) + 8 * (n16 & 1) + ((fv(vkey) >> 1) << 5);
 
   const float c = fmaxf(a.scale_log2, 1.17549435e-38f);
-  auto compute = [&](auto bc, int kv0) {
+  // S^T = K Q^T of the tile in buffer b over NSUB key subtiles of 16
+  auto qk = [&](auto bc, f32x4 (&sacc)[NQ][NSUB]) {
     constexpr int b = decltype(bc)::value;
-    // S^T = K Q^T over NSUB key subtiles of 16
-    f32x4 sacc[NQ][NSUB];
 #pragma unroll
     for (int g = 0; g < NQ; ++g)
 #pragma unroll
@@ -305,7 +368,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
         for (int g = 0; g < NQ; ++g) sacc[g][sub] = mfma16<DT>(ka, qf[g][ks], sacc[g][sub]);
       }
     }
-    // online softmax; lane holds query n16, keys kv0 + 16*sub + 4*g4 + i.
+  };
+  // online softmax of the scores of keys kv0 .. kv0+KT-1 into the P^T
+  // operands (pb, and the bf16 remainders pbl); lane holds query n16, keys
+  // kv0 + 16*sub + 4*g4 + i.
+  auto softmax = [&](f32x4 (&sacc)[NQ][NSUB], int kv0, u32x4 (&pb)[NQ][NKST], u32x4 (&pbl)[NQ][NKST]) {
     // Only tiles that reach past the wave's first query need the causal
     // mask (wave-uniform test). The running max is raised lazily: a row
     // keeps its reference max until a tile's max exceeds it by more than
@@ -324,9 +391,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
             if (kv0 + 16 * sub + 4 * g4 + i > last_key) sacc[g][sub][i] = -INFINITY;
       }
     }
-    u32x4 pb[NQ][NKST];
-    u32x4 pbl[NQ][NKST];  // bf16 remainders
-    static_assert(NQ == 2, "row maxima of the two query groups are taken together");
+    static_assert(NQ == 1 || NQ == 2, "one or two query groups per wave");
     float mrow[NQ];  // max of the raw scores (c > 0: the scaled max is mr * c)
 #pragma unroll
     for (int g = 0; g < NQ; ++g) {
@@ -346,7 +411,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
 #pragma unroll
     for (int g = 0; g < NQ; ++g) jump |= mrow[g] * c > m[g] + RESCALE_LOG2;
     if (__any(jump)) {
-      rows4_max2(mrow[0], mrow[1]);
+      if constexpr (NQ == 2) rows4_max2(mrow[0], mrow[1]);
+      else mrow[0] = rows4_max(mrow[0]);
 #pragma unroll
       for (int g = 0; g < NQ; ++g) {
         const float mt = mrow[g] * c;
@@ -387,20 +453,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
         }
       }
     }
-    // O^T += V^T P^T: A = V^T rows d = 16*dt + n16, keys 4*g4 + {0..3} and 16 + 4*g4 + {0..3}, two
-    // transposing 8-byte LDS reads (each 16 lanes turn 4 key rows x 16 dims around)
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
+  };
+  // O^T += V^T P^T with the V tile in buffer b: A = V^T rows d = 16*dt + n16, keys 4*g4 + {0..3} and
+  // 16 + 4*g4 + {0..3}, two transposing 8-byte LDS reads (each 16 lanes turn 4 key rows x 16 dims around)
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  auto vt_frag = [&](auto bc, int dt) -> u32x4 {
+    constexpr int b = decltype(bc)::value;
     const uint8_t* vb = &sv[b][0];
+    const uint32_t off = v_rd ^ (dt << 5);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) void*)(vb + off));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) void*)(vb + off + 16 * ROWB));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+    const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2[0], l2[1], h2[0], h2[1]};
+  };
+  auto pv = [&](auto bc, const u32x4 (&pb)[NQ][NKST], const u32x4 (&pbl)[NQ][NKST]) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const uint32_t off = v_rd ^ (dt << 5);
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) void*)(vb + off));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) void*)(vb + off + 16 * ROWB));
-      const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-      const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
-      const u32x4 va = u32x4{l2[0], l2[1], h2[0], h2[1]};
+      const u32x4 va = vt_frag(bc, dt);
 #pragma unroll
       for (int g = 0; g < NQ; ++g) {
         o[g][dt] = mfma16<DT>(va, pb[g][0], o[g][dt]);
@@ -414,6 +486,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
         lacc[g] = mfma16<DT>(ones, pb[g][kst], lacc[g]);
         if constexpr (DT == Dt::BF16) lacc[g] = mfma16<DT>(ones, pbl[g][kst], lacc[g]);
       }
+  };
+  auto compute = [&](auto bc, int kv0) {
+    f32x4 sacc[NQ][NSUB];
+    u32x4 pb[NQ][NKST], pbl[NQ][NKST];
+    qk(bc, sacc);
+    softmax(sacc, kv0, pb, pbl);
+    pv(bc, pb, pbl);
   };
 
   // Pipeline over tiles with three LDS buffers: tile t+2's DMA is issued
@@ -430,39 +509,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qf[g][ks]));
   const int last = n_tiles - 1;
-  {
-    int p0[PPW], p1[PPW];
+  // prologue: tiles 0 .. NBUF-2 into buffers 0 .. NBUF-2 (clamped to the
+  // last tile; a buffer past it holds a copy that is never read)
+#pragma unroll
+  for (int i = 0; i + 1 < NBUF; i += 2) {
+    int pa_ids[PPW], pb_ids[PPW];
+    const int ta = min(i, last), tb = min(i + 1, last);
     if constexpr (PPW == 2) {
-      sload2(entry(0, 0), entry(0, 1), p0[0], p0[1]);
-      sload2(entry(min(1, last), 0), entry(min(1, last), 1), p1[0], p1[1]);
+      sload2(entry(ta, 0), entry(ta, 1), pa_ids[0], pa_ids[1]);
+      if (i + 2 < NBUF) sload2(entry(tb, 0), entry(tb, 1), pb_ids[0], pb_ids[1]);
     } else {
-      sload2(entry(0, 0), entry(min(1, last), 0), p0[0], p1[0]);
+      sload2(entry(ta, 0), entry(tb, 0), pa_ids[0], pb_ids[0]);
     }
-    dma_ids(0, 0, p0);
-    dma_ids(min(1, last), 1, p1);
+    dma_ids(ta, i, pa_ids);
+    if (i + 2 < NBUF) dma_ids(tb, i + 1, pb_ids);
   }
-  // one iteration, buffer b = t mod 3 known at compile time (the loop is
-  // unrolled three times), so LDS offsets are immediates
+  // One iteration, buffer b = t mod NBUF known at compile time (the loop is
+  // unrolled NBUF times), so LDS offsets are immediates. Tile t+NBUF-1 goes
+  // into the buffer of tile t-1, which every wave has finished once past
+  // this iteration's barrier; clamped re-reads of the last tile land in
+  // buffers no later iteration reads.
   auto iter = [&](int t, auto bc) {
     constexpr int b = decltype(bc)::value;
-    const int tn = min(t + 2, last);
+    const int tn = min(t + NBUF - 1, last);
     const int32_t* e[PPW];
     int ids[PPW];
 #pragma unroll
     for (int i = 0; i < PPW; ++i) e[i] = entry(tn, i);
-    sload_barrier<PPW>(e, ids);
+    sload_barrier<PPW, 2 * PPW * (NBUF - 2)>(e, ids);
     if ((t + 1) * KT > kv_end) {
       zero_tail(t, b);
       __syncthreads();
     }
-    dma_ids(tn, (b + 2) % NBUF, ids);
+    dma_ids(tn, (b + NBUF - 1) % NBUF, ids);
     if (wave_active && t * KT <= wave_last_pos) compute(bc, t * KT);
   };
-  for (int t = 0; t < n_tiles; t += 3) {
-    iter(t, std::integral_constant<int, 0>{});
-    if (t + 1 < n_tiles) iter(t + 1, std::integral_constant<int, 1>{});
-    if (t + 2 < n_tiles) iter(t + 2, std::integral_constant<int, 2>{});
-  }
+  for (int t = 0; t < n_tiles; t += NBUF)
+    for_each_const(
+        [&](auto bc) {
+          if (t + decltype(bc)::value < n_tiles) iter(t + decltype(bc)::value, bc);
+        },
+        std::make_integer_sequence<int, NBUF>{});
   wait_vmcnt0();  // no DMA may still be writing this workgroup's LDS when it ends
 
   if (!wave_active) return;
@@ -497,7 +584,7 @@ static hipError_t launch_k4(const PrefillArgs& a, hipStream_t stream) {
   const int64_t pairs = (int64_t)a.num_seqs * a.H;
   const int64_t grid = (int64_t)a.q_tiles * (a.grouped ? (pairs + 7) / 8 * 8 : pairs);
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((prefill_mfma_kernel<DT, D, BS>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((prefill_mfma_kernel<DT, D, BS>), dim3((unsigned)grid), dim3(PfShape<D>::NW * 64), 0, stream, a);
   return hipGetLastError();
 }
 
