@@ -32,8 +32,9 @@
 //   * online softmax per query: the max over the raw scores (the scale is
 //     applied once to it, and inside the exponent's FMA), cross-row max on
 //     the row-swap instructions (both query groups folded together), P
-//     narrowed with the packed converts; the
-//     denominator is summed on the matrix cores (a block of ones in V^T);
+//     narrowed with the packed converts; each lane sums the rounded P of
+//     its own keys into the denominator with packed dot2 against (1, 1),
+//     and the four lanes of a query add their sums at the end;
 //     only tiles that cross a wave's first query carry the causal mask (the
 //     masked scores are set to -inf), tiles past its last query are skipped, and
 //     the running max is raised lazily (see compute()) so the accumulators
@@ -153,6 +154,13 @@ __device__ __forceinline__ void sload_barrier(const int32_t* const (&e)[PPW], in
 template <typename F, int... B>
 __device__ __forceinline__ void for_each_const(F&& f, std::integer_sequence<int, B...>) {
   (f(std::integral_constant<int, B>{}), ...);
+}
+// c + the two 16-bit values of w times those of one2 (packed f16 or bf16)
+template <Dt DT> __device__ __forceinline__ float dot2one(uint32_t w, uint32_t one2, float c) {
+  if constexpr (DT == Dt::F16)
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w), __builtin_bit_cast(half2_t, one2), c, false);
+  else
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, w), __builtin_bit_cast(bf162_t, one2), c, false);
 }
 template <typename T> __device__ __forceinline__ uint32_t lds_offset(T* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)p;
@@ -290,20 +298,19 @@ __global__ __launch_bounds__(PfShape<D>::NW * 64) __attribute__((amdgpu_waves_pe
     }
   }
 
-  // o: O^T of the wave's queries; lacc: the softmax denominators, summed on
-  // the matrix cores as a 17th row block of ones in V^T (every row of lacc
-  // holds the sum of the query's rounded P, the same P the numerator uses)
-  f32x4 o[NQ][NDT], lacc[NQ];
-  float m[NQ];
+  // o: O^T of the wave's queries; lsum: this lane's share of the softmax
+  // denominators (the sum of the rounded P of its keys, the same P the
+  // numerator uses), added over the query's four lanes at the end
+  f32x4 o[NQ][NDT];
+  float m[NQ], lsum[NQ];
 #pragma unroll
   for (int g = 0; g < NQ; ++g) {
     m[g] = -INFINITY;
-    lacc[g] = zero4();
+    lsum[g] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[g][dt] = zero4();
   }
   constexpr uint32_t ONE2 = ones2<DT>();
-  const u32x4 ones = u32x4{ONE2, ONE2, ONE2, ONE2};
 
   // DMA of one tile into LDS buffer b: piece p holds rows p*PR .. p*PR+PR-1
   // and wave w loads pieces w, w+4, ...; lane L of a piece fills chunk
@@ -420,7 +427,7 @@ __global__ __launch_bounds__(PfShape<D>::NW * 64) __attribute__((amdgpu_waves_pe
         if (__any(grow)) {
           const float m_new = grow ? mt : m[g];
           const float alpha = __builtin_amdgcn_exp2f(m[g] - m_new);
-          lacc[g] *= alpha;
+          lsum[g] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) o[g][dt] *= alpha;
           m[g] = m_new;
@@ -443,6 +450,8 @@ __global__ __launch_bounds__(PfShape<D>::NW * 64) __attribute__((amdgpu_waves_pe
 #pragma unroll
         for (int j = 0; j < 4; ++j) w[j] = pack2<DT>(p[8 * kst + 2 * j], p[8 * kst + 2 * j + 1]);
         pb[g][kst] = u32x4{w[0], w[1], w[2], w[3]};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lsum[g] = dot2one<DT>(w[j], ONE2, lsum[g]);
         if constexpr (DT == Dt::BF16) {
           uint32_t r[4];
 #pragma unroll
@@ -450,6 +459,8 @@ __global__ __launch_bounds__(PfShape<D>::NW * 64) __attribute__((amdgpu_waves_pe
             r[j] = pack2<DT>(p[8 * kst + 2 * j] - __uint_as_float(w[j] << 16),
                              p[8 * kst + 2 * j + 1] - __uint_as_float(w[j] & 0xffff0000u));
           pbl[g][kst] = u32x4{r[0], r[1], r[2], r[3]};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) lsum[g] = dot2one<DT>(r[j], ONE2, lsum[g]);
         }
       }
     }
@@ -469,30 +480,24 @@ __global__ __launch_bounds__(PfShape<D>::NW * 64) __attribute__((amdgpu_waves_pe
     const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
     return u32x4{l2[0], l2[1], h2[0], h2[1]};
   };
-  auto pv = [&](auto bc, const u32x4 (&pb)[NQ][NKST], const u32x4 (&pbl)[NQ][NKST]) {
+  auto pv = [&](auto bc, const u32x4 (&pb)[NQ][NKST], const u32x4 (&pbl)[NQ][NKST], const u32x4 va0) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const u32x4 va = vt_frag(bc, dt);
+      const u32x4 va = dt == 0 ? va0 : vt_frag(bc, dt);
 #pragma unroll
       for (int g = 0; g < NQ; ++g) {
         o[g][dt] = mfma16<DT>(va, pb[g][0], o[g][dt]);
         if constexpr (DT == Dt::BF16) o[g][dt] = mfma16<DT>(va, pbl[g][0], o[g][dt]);
       }
     }
-#pragma unroll
-    for (int kst = 0; kst < NKST; ++kst)
-#pragma unroll
-      for (int g = 0; g < NQ; ++g) {
-        lacc[g] = mfma16<DT>(ones, pb[g][kst], lacc[g]);
-        if constexpr (DT == Dt::BF16) lacc[g] = mfma16<DT>(ones, pbl[g][kst], lacc[g]);
-      }
   };
   auto compute = [&](auto bc, int kv0) {
     f32x4 sacc[NQ][NSUB];
     u32x4 pb[NQ][NKST], pbl[NQ][NKST];
     qk(bc, sacc);
+    const u32x4 va0 = vt_frag(bc, 0);  // read ahead: its LDS latency hides under the softmax
     softmax(sacc, kv0, pb, pbl);
-    pv(bc, pb, pbl);
+    pv(bc, pb, pbl, va0);
   };
 
   // Pipeline over tiles with three LDS buffers: tile t+2's DMA is issued
@@ -553,10 +558,11 @@ __global__ __launch_bounds__(PfShape<D>::NW * 64) __attribute__((amdgpu_waves_pe
   wait_vmcnt0();  // no DMA may still be writing this workgroup's LDS when it ends
 
   if (!wave_active) return;
-  // finish: every row of lacc holds the query's denominator
+  // finish: the query's denominator is the sum over its four lanes
 #pragma unroll
   for (int g = 0; g < NQ; ++g) {
-    const float lt = lacc[g][0];
+    const float l2 = lsum[g] + __shfl_xor(lsum[g], 16);
+    const float lt = l2 + __shfl_xor(l2, 32);
     const int jq = wq0 + g * 16 + n16;
     if (jq >= L) continue;
     const int64_t orow = ((int64_t)(q_beg + jq) * a.H + h) * D;
