@@ -21,6 +21,10 @@ Other workloads (``--workload``), same machinery:
               4096 rows, then causal prefill of 8 chunks of 512 queries after
               1536 cached tokens (150 GFLOP): the compute-bound path, reported
               in TFLOP/s against the dense MFMA peak
+  prefill_f32 the mixed step's cache write and its 4 prefill chunks with f32
+              caches and queries: the f32 prefill, one decode wave per query
+              row (each row re-reads its causal prefix), in TFLOP/s against
+              the fp32 vector peak
 
 One step = the workload's whole path, all inputs resident in HBM:
 reshape_and_cache of the step's new tokens, [prefill,] then split-K decode
@@ -54,6 +58,9 @@ METRIC = "paged decode attention achieved HBM GB/s (% of peak) at LLaMA-7B layer
 METRIC_OTHER = "paged attention step achieved HBM GB/s (% of peak)"
 HBM_PEAK_GBPS = 8000.0
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # dense fp16/bf16 matrix-core peak of MI355X
+# fp32 vector peak: 256 CUs x 4 SIMDs x 16 lanes x 2 (FMA) x 2 (packed FP32) x 2.4 GHz
+F32_VALU_PEAK_TFLOPS = 157.3
+PREFILL_WORKLOADS = ("prefill_long", "prefill_f32")
 KERNEL_SOURCES = ["pa_decode.hip", "pa_decode_device.h", "pa_device.h", "pa_bounds.h", "pa_internal.h"]
 SHARED_KERNEL_SOURCES = KERNEL_SOURCES + ["pa_shared.hip"]
 PREFILL_KERNEL_SOURCES = ["pa_prefill.hip", "pa_device.h", "pa_bounds.h", "pa_internal.h"]
@@ -73,13 +80,16 @@ WORKLOADS = {
                   "seed 396",
     "prefill_long": "prefill_long: reshape_and_cache of the chunks' 4096 rows + causal prefill of 8 chunks of 512 "
                     "queries after 1536 cached tokens, 40 heads x 128, f16, block_size 16, seed 397",
+    "prefill_f32": "prefill_f32: reshape_and_cache of the mixed step's 2048 rows + causal prefill of its 4 chunks "
+                   "(L U[256,512], prior U[0,1024]), 40 heads x 128, f32, block_size 16, seed 396",
 }
 PREFILL_METRIC = "causal paged prefill achieved TFLOP/s (% of the dense MFMA peak)"
+PREFILL_F32_METRIC = "causal paged prefill achieved TFLOP/s (% of the fp32 vector peak)"
 
 
 def traffic_file(workload, shared=False):
-    if workload == "prefill_long":
-        return os.path.join(ROOT, "profiles", "prefill_long_traffic.json")
+    if workload in PREFILL_WORKLOADS:
+        return os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
     tag = workload + ("_shared" if shared else "_plain" if workload == "prefix13b" else "")
     return os.path.join(ROOT, "profiles", f"decode_{tag}_traffic.json")
 
@@ -280,8 +290,10 @@ def cpu_baseline(wl, threads, alg_bytes, sample_bytes):
             "host": {"cpu_model": model, "usable_cores": avail}}
 
 
-def prefill_config():
-    from workloads import prefill_workload
+def prefill_config(workload="prefill_long"):
+    from workloads import config5, prefill_workload
+    if workload == "prefill_f32":
+        return config5(dtype="f32")
     return prefill_workload("prefill_long", 397, "f16", 40, 128, 16, [1536] * 8, [512] * 8, maxb=128)
 
 
@@ -342,7 +354,7 @@ def prefill_main(args):
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     t = time.time()
-    wl = prefill_config()
+    wl = prefill_config(args.workload)
     p = wl.prefill
     log(f"[bench] {args.workload}: generated in {time.time() - t:.1f}s: {wl.num_blocks} blocks, {p.total_q} queries")
     od = OnDevice(wl)
@@ -417,7 +429,8 @@ def prefill_main(args):
         if not graph_ok:
             raise SystemExit("graph replay disagrees with the eager step")
 
-    peak = MFMA_PEAK_TFLOPS[wl.dtype]
+    f32 = wl.dtype == "f32"
+    peak = F32_VALU_PEAK_TFLOPS if f32 else MFMA_PEAK_TFLOPS[wl.dtype]
     cold_ms = float(cold_pf.mean())
     pf_tflops = flops / (cold_ms * 1e-3) / 1e12
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -458,7 +471,7 @@ def prefill_main(args):
                "host": {"cpu_model": model, "usable_cores": avail}}
 
     rec = {
-        "metric": PREFILL_METRIC,
+        "metric": PREFILL_F32_METRIC if f32 else PREFILL_METRIC,
         "value": round(value, 1),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -473,9 +486,10 @@ def prefill_main(args):
         "config": {"workload": WORKLOADS[args.workload], "global_batch": int(p.num_seqs),
                    "seq_len": int(p.max_context_len), "parallelism": "none (1 GPU)"},
         "pct_of_peak": round(100 * value / peak, 2),
-        "roofline": {"bound": "mfma", "achieved": round(pf_tflops, 1), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(pf_tflops / peak, 4), "traffic": traffic,
-                     "kernel": f"prefill_mfma_kernel<{wl.dtype},{D},{wl.block_size}>",
+        "roofline": {"bound": "alu" if f32 else "mfma", "achieved": round(pf_tflops, 1), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(pf_tflops / peak, 4), "traffic": traffic,
+                     "kernel": (f"decode_partition_kernel<f32,{D},{wl.block_size},PrefillRows>" if f32 else
+                                f"prefill_mfma_kernel<{wl.dtype},{D},{wl.block_size}>"),
                      "flops_per_launch": flops, "bytes_per_launch": pf_bytes,
                      "avg_launch_us": round(cold_ms * 1e3, 2),
                      "timing": f"HIP events on the launch stream around each of {args.steps} eager launches, "
@@ -484,6 +498,9 @@ def prefill_main(args):
                      "launch_us": pct(cold_pf), "warm_avg_launch_us": round(pf_ms * 1e3, 2),
                      "hbm_frac": round(pf_bytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                      "roofline_us": round(max(flops / (peak * 1e12), pf_bytes / (HBM_PEAK_GBPS * 1e9)) * 1e6, 2)},
+        # f32: each query row is its own decode over its causal prefix, so the
+        # K/V bytes it reads grow with L x ctx instead of ctx
+        "row_path_kv_bytes": (flops // (4 * D)) * D * elt * 2 if f32 else None,
         "timing": "hip_graph_replay" if not args.eager else "eager",
         "eager_ms_per_step": round(eager_ms, 5),
         "hbm_copy_probe_GBps": round(copy_gbps, 1),
@@ -525,9 +542,9 @@ def main():
     # no garbage-collection pause of the host inside the timed launches
     gc.collect()
     gc.disable()
-    if args.workload == "prefill_long":
+    if args.workload in PREFILL_WORKLOADS:
         if args.block_size is not None or args.plain:
-            raise SystemExit("--block-size and --plain do not apply to prefill_long")
+            raise SystemExit(f"--block-size and --plain do not apply to {args.workload}")
         prefill_main(args)
         return
 
