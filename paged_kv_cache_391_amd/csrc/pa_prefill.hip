@@ -27,8 +27,9 @@
 //     turns 4 key rows x 16 dims around per 16 lanes) use every bank once;
 //   * only the last tile is clamped (its rows past the context read the
 //     last block) and has its V rows past the context zeroed in LDS;
-//   * each wave owns NQ groups of 16 queries; every K or V^T fragment read
-//     from LDS feeds one MFMA per group;
+//   * each wave owns NQ groups of 16 queries (two in the standard shape, one
+//     in the wide shape, below); every K or V^T fragment read from LDS
+//     feeds one MFMA per group;
 //   * online softmax per query: the max over the raw scores (the scale is
 //     applied once to it, and inside the exponent's FMA), cross-row max on
 //     the row-swap instructions (both query groups folded together), P
@@ -56,27 +57,25 @@ namespace {
 #ifndef PA_PREFILL_KT
 #define PA_PREFILL_KT 32
 #endif
-#ifndef PA_PREFILL_NQ
-#define PA_PREFILL_NQ 2
-#endif
 constexpr int KT = PA_PREFILL_KT;  // keys per tile (32 or 64)
-#ifndef PA_PREFILL_NW
-#define PA_PREFILL_NW 4
-#endif
-#ifndef PA_PREFILL_WAVES
-#define PA_PREFILL_WAVES 3
-#endif
-// Shape per head dim: NW waves per workgroup, NQ 16-query groups per wave;
-// every shape covers QT queries per workgroup.
-template <int D> struct PfShape {
-  static constexpr int NW = D == 128 ? PA_PREFILL_NW : 4;
-  static constexpr int NQ = D == 128 ? PA_PREFILL_NQ : 2;
+// Workgroup shapes: NW waves, NQ 16-query groups per wave, every shape
+// covering QT queries per workgroup. The standard shape (4 waves x 32
+// queries, three waves per SIMD) reads each K or V^T fragment from LDS once
+// for two MFMAs, the best rate when there are more workgroups than the chip
+// holds at once. The wide shape (8 waves x 16 queries, head dim 128 only)
+// halves each wave's dependent chain per tile (half the MFMAs and
+// exponentials, four waves per SIMD) at twice the LDS reads per MFMA; it
+// shortens the longest query tiles when every workgroup is resident at once.
+template <int D, bool WIDE> struct PfShape {
+  static constexpr bool W = WIDE && D == 128;
+  static constexpr int NW = W ? 8 : 4;
+  static constexpr int NQ = W ? 1 : 2;
   static constexpr int QW = 16 * NQ;  // queries per wave
   static constexpr int QT = NW * QW;  // queries per workgroup
-  static constexpr int WAVES = D == 128 ? PA_PREFILL_WAVES : 3;  // waves per SIMD the registers must allow
+  static constexpr int WAVES = W ? 4 : 3;  // waves per SIMD the registers must allow
 };
-constexpr int QT = PfShape<128>::QT;
-static_assert(PfShape<64>::QT == QT, "one query tile for every head dim");
+constexpr int QT = PfShape<128, false>::QT;
+static_assert(PfShape<64, false>::QT == QT && PfShape<128, true>::QT == QT, "one query tile for every shape");
 #ifndef PA_PREFILL_NBUF
 #define PA_PREFILL_NBUF 3
 #endif
@@ -168,9 +167,11 @@ template <typename T> __device__ __forceinline__ uint32_t lds_offset(T* p) {
 
 }  // namespace
 
-template <Dt DT, int D, int BS>
-__global__ __launch_bounds__(PfShape<D>::NW * 64) __attribute__((amdgpu_waves_per_eu(PfShape<D>::WAVES))) void prefill_mfma_kernel(const PrefillArgs a) {
-  constexpr int NW = PfShape<D>::NW, NQ = PfShape<D>::NQ, QW = PfShape<D>::QW;
+template <Dt DT, int D, int BS, bool WIDE>
+__global__ __launch_bounds__((PfShape<D, WIDE>::NW * 64))
+    __attribute__((amdgpu_waves_per_eu(PfShape<D, WIDE>::WAVES))) void prefill_mfma_kernel(const PrefillArgs a) {
+  using Shape = PfShape<D, WIDE>;
+  constexpr int NW = Shape::NW, NQ = Shape::NQ, QW = Shape::QW;
   constexpr int KS = D / 32;     // MFMA k-steps over head_dim for Q.K
   constexpr int NDT = D / 16;    // 16-row tiles of O^T
   constexpr int NSUB = KT / 16;  // 16-key subtiles of S^T
@@ -590,7 +591,16 @@ static hipError_t launch_k4(const PrefillArgs& a, hipStream_t stream) {
   const int64_t pairs = (int64_t)a.num_seqs * a.H;
   const int64_t grid = (int64_t)a.q_tiles * (a.grouped ? (pairs + 7) / 8 * 8 : pairs);
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((prefill_mfma_kernel<DT, D, BS>), dim3((unsigned)grid), dim3(PfShape<D>::NW * 64), 0, stream, a);
+  // every workgroup resident at once: the wide shape (head dim 128)
+  if constexpr (D == 128) {
+    if (!a.grouped) {
+      hipLaunchKernelGGL((prefill_mfma_kernel<DT, D, BS, true>), dim3((unsigned)grid), dim3(PfShape<D, true>::NW * 64),
+                         0, stream, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((prefill_mfma_kernel<DT, D, BS, false>), dim3((unsigned)grid), dim3(PfShape<D, false>::NW * 64), 0,
+                     stream, a);
   return hipGetLastError();
 }
 

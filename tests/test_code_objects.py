@@ -63,15 +63,18 @@ def test_no_kernel_uses_scratch(tmp_path):
 
 def test_hot_kernels_keep_their_occupancy(tmp_path):
     """512 VGPRs per SIMD lane: five waves per SIMD for the f16/bf16 decode
-    partitions (<= 96 VGPRs, granularity 8), three for the prefill and the
-    f32 decode at head dim 128 (<= 168)."""
+    partitions (<= 96 VGPRs, granularity 8), three for the prefill's
+    standard shape and the f32 decode at head dim 128 (<= 168), four for the
+    prefill's wide shape (<= 128)."""
     ks = _kernels(tmp_path)
     dec16 = [m for n, m in ks.items() if "decode_partition_kernel" in n and re.search(r"DtE[12]E", n)]
     dec32 = [m for n, m in ks.items() if "decode_partition_kernel" in n and "DtE0ELi128" in n]
     pf = [m for n, m in ks.items() if "prefill_mfma_kernel" in n]
-    assert dec16 and dec32 and pf
+    wide = [m for n, m in ks.items() if "prefill_mfma_kernel" in n and "ELb1E" in n]
+    assert dec16 and dec32 and pf and wide
     assert max(m["vgpr_count"] for m in dec16) <= 96
     assert max(m["vgpr_count"] for m in dec32) <= 168
     assert max(m["vgpr_count"] for m in pf) <= 168
+    assert max(m["vgpr_count"] for m in wide) <= 128
     # the prefill's three LDS buffers per operand (48 KiB) let three workgroups share a CU's 160 KiB
     assert max(m["group_segment_fixed_size"] for m in pf) <= 160 * 1024 // 3

@@ -642,7 +642,8 @@ def test_prefill_many_workgroups_grouped_order(dtype, D, bs):
     together, in groups of 8 pairs (195 pairs leave a partial group). Every
     output element against the oracle, and the first two chunks bit-identical to a call
     that holds only them (104 workgroups, every one resident at once: the
-    plain order)."""
+    plain order, run by the kernel's wide shape of 8 waves x 16 queries
+    where head dim is 128)."""
     rng = np.random.default_rng(11)
     prior = [int(x) for x in rng.integers(0, 600, 15)]
     chunk = [int(x) for x in rng.integers(385, 513, 15)]
