@@ -138,7 +138,6 @@ pa_status prepare_decode(DecodeCall& call, void* out, pa_dtype out_dtype, const 
   a.v_cache = v_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  a.query_start_loc = nullptr;
   a.num_rows = num_seqs;
   a.num_seqs = num_seqs;
   a.H = num_heads;
@@ -396,13 +395,10 @@ pa_status pa_paged_attention_decode_shared_prefix(
   return hip_status(e);
 }
 
-// Validated launch plan of one prefill call: the MFMA kernel (f16/bf16) or
-// the per-query-row vector path (f32).
+// Validated launch plan of one prefill call: the MFMA kernel of its dtype.
 struct PrefillCall {
-  bool mfma = false;
   bool empty = true;
   pa::PrefillArgs pf{};
-  pa::DecodeArgs rows{};
   Dt dt = Dt::F16;
   int D = 0, BS = 0;
 };
@@ -427,68 +423,42 @@ static pa_status prepare_prefill(PrefillCall& call, void* out, pa_dtype out_dtyp
   if (call.empty) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc)
     return PA_ERR_INVALID_ARG;
-  const float scale_log2 = scale * 1.4426950408889634f;
   call.dt = static_cast<Dt>(dtype);
   call.D = head_dim;
   call.BS = block_size;
-  call.mfma = dtype != PA_F32;
-  if (call.mfma) {
-    pa::PrefillArgs& a = call.pf;
-    a.out = out;
-    a.q = q;
-    a.k_cache = k_cache;
-    a.v_cache = v_cache;
-    a.block_tables = block_tables;
-    a.context_lens = context_lens;
-    a.query_start_loc = query_start_loc;
-    a.num_seqs = num_seqs;
-    a.total_q = total_q;
-    a.H = num_heads;
-    a.max_blocks = max_blocks_per_seq;
-    a.max_context_len = max_context_len;
-    a.num_blocks = num_blocks;
-    a.q_tiles = (int)ceil_div(max_q_len, pa::prefill_mfma_q_tile());
-    // a negative scale runs as |scale| on negated queries (a sign flip, exact)
-    a.scale_log2 = std::fabs(scale) * 1.4426950408889634f;
-    a.q_sign = std::signbit(scale) ? 0x80008000u : 0u;
-    a.out_f32 = out_dtype == PA_F32 ? 1 : 0;
-    if ((int64_t)a.q_tiles * num_heads * (num_seqs + 7) > INT32_MAX) return PA_ERR_INVALID_ARG;
-    // more workgroups than the chip holds at once: group each pair's query
-    // tiles for L2 reuse (the kernel's work-order note)
-    const int cus = device_compute_units();
-    a.cus = cus;
-    a.grouped = cus > 0 && (int64_t)a.q_tiles * num_heads * num_seqs > (int64_t)cus * pa::kPrefillWorkgroupsPerCU;
-    return PA_OK;
-  }
-  // fp32: every query row is a decode over its own causal prefix
-  if ((int64_t)total_q * num_heads > INT32_MAX) return PA_ERR_INVALID_ARG;
-  pa::DecodeArgs& a = call.rows;
+  pa::PrefillArgs& a = call.pf;
   a.out = out;
-  a.ws = nullptr;
   a.q = q;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.query_start_loc = query_start_loc;
-  a.num_rows = total_q;
   a.num_seqs = num_seqs;
+  a.total_q = total_q;
   a.H = num_heads;
   a.max_blocks = max_blocks_per_seq;
-  a.max_ctx = max_context_len;
+  a.max_context_len = max_context_len;
   a.num_blocks = num_blocks;
-  a.max_parts = 1;
-  a.ws_parts = 1;
-  a.part_tiles = pa::single_partition_tiles(max_context_len);
-  a.scale_log2 = scale_log2;
-  a.out_f32 = 1;
+  a.q_tiles = (int)ceil_div(max_q_len, pa::prefill_mfma_q_tile());
+  // a negative scale runs as |scale| on negated queries (a sign flip, exact)
+  a.scale_log2 = std::fabs(scale) * 1.4426950408889634f;
+  a.q_sign = std::signbit(scale) ? 0x80008000u : 0u;
+  a.out_f32 = out_dtype == PA_F32 ? 1 : 0;
+  if ((int64_t)a.q_tiles * num_heads * (num_seqs + 7) > INT32_MAX) return PA_ERR_INVALID_ARG;
+  // more workgroups than the chip holds at once: group each pair's query
+  // tiles for L2 reuse (the kernel's work-order note)
+  const int cus = device_compute_units();
+  a.cus = cus;
+  const int per_cu = dtype == PA_F32 ? pa::kPrefillF32WorkgroupsPerCU : pa::kPrefillWorkgroupsPerCU;
+  a.grouped = cus > 0 && (int64_t)a.q_tiles * num_heads * num_seqs > (int64_t)cus * per_cu;
   return PA_OK;
 }
 
 static hipError_t launch_prefill(const PrefillCall& call, hipStream_t stream) {
   if (call.empty) return hipSuccess;
-  if (call.mfma) return pa::launch_prefill_mfma(call.pf, call.dt, call.D, call.BS, stream);
-  return pa::launch_decode_partitions(call.rows, Dt::F32, call.D, call.BS, pa::RowMode::PrefillRows, stream);
+  if (call.dt == Dt::F32) return pa::launch_prefill_f32(call.pf, call.D, call.BS, stream);
+  return pa::launch_prefill_mfma(call.pf, call.dt, call.D, call.BS, stream);
 }
 
 pa_status pa_paged_attention_prefill(void* out, pa_dtype out_dtype, const void* q, const void* k_cache,

@@ -148,7 +148,6 @@ template <Dt DT>
 static hipError_t dispatch_k2_mode(const DecodeArgs& a, int D, int BS, RowMode mode, hipStream_t stream) {
   switch (mode) {
     case RowMode::Decode: return dispatch_k2<DT, RowMode::Decode>(a, D, BS, stream);
-    case RowMode::PrefillRows: return dispatch_k2<DT, RowMode::PrefillRows>(a, D, BS, stream);
     case RowMode::SharedTail: break;  // tails run inside the shared-prefix step kernel only
   }
   return hipErrorInvalidValue;

@@ -142,20 +142,6 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float x, int o
 // Context length of row r (decode and shared-tail modes), clamped.
 __device__ __forceinline__ int row_ctx(const DecodeArgs& a, int r) { return clamp_len(a.context_lens[r], a.max_ctx); }
 
-// Row r of the prefill-row mode is query j of chunk s: its causal context is
-// ctx[s] - L_s + j + 1 tokens of sequence s (clamped like any length).
-__device__ __forceinline__ void prefill_row(const DecodeArgs& a, int r, int& seq, int& ctx) {
-  const int32_t* qsl = a.query_start_loc;
-  int lo = 0, hi = a.num_seqs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (qsl[mid] <= r) lo = mid; else hi = mid - 1;
-  }
-  seq = lo;
-  const int L = qsl[lo + 1] - qsl[lo];
-  ctx = clamp_len(a.context_lens[lo] - L + (r - qsl[lo]) + 1, a.max_ctx);
-}
-
 // Group g of a prefix-sharing batch is rows group_starts[g] .. group_starts[g+1]-1.
 // The starts are non-decreasing from group_starts[0] = 0, so the group is
 // the number of starts g >= 1 at or before row r. The wave counts them 64 at
@@ -236,13 +222,8 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int b
   const int h = hg * HG + wave;
   if (h >= a.H) return;
 
-  int seq, ctx;
-  if constexpr (MODE == RowMode::PrefillRows) {
-    prefill_row(a, row, seq, ctx);
-  } else {
-    seq = row;
-    ctx = row_ctx(a, row);
-  }
+  const int seq = row;
+  const int ctx = row_ctx(a, row);
   const int n_tiles = (ctx + 15) >> 4;
   const RowParts rp = row_parts<MODE>(a, row, ctx);
   // partition 0 of an empty row still runs (it writes zeros), except for the

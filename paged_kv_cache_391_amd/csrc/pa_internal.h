@@ -50,7 +50,6 @@ inline int shared_partition_tokens(int block_size) {
 // Which rows a partition-kernel launch walks.
 enum class RowMode : int {
   Decode = 0,       // row s = sequence s, tokens [0, ctx)
-  PrefillRows = 1,  // row r = one query of a causal chunk, tokens [0, its position]
   SharedTail = 2,   // row s = sequence s of a prefix-sharing group, tokens [prefix, ctx)
 };
 
@@ -62,8 +61,7 @@ struct DecodeArgs {
   const void* v_cache;
   const int32_t* block_tables;      // [num_seqs][max_blocks]
   const int32_t* context_lens;      // [num_seqs]
-  const int32_t* query_start_loc;   // [num_seqs+1], prefill-row mode only
-  int num_rows;                     // decode: num_seqs; prefill-row mode: total queries
+  int num_rows;                     // rows of the launch (one per sequence)
   int num_seqs;
   int H;
   int max_blocks;
@@ -103,7 +101,7 @@ hipError_t launch_shared_prefix_step(const DecodeArgs& a, Dt dt, int D, int BS, 
                                      hipStream_t stream);
 constexpr int kSharedMembersPerWave = 16;
 
-// MFMA causal prefill (K4), fp16/bf16 only
+// MFMA causal prefill: K4 (fp16/bf16) and its fp32 form
 struct PrefillArgs {
   void* out;                        // [total_q][H][D]
   const void* q;                    // [total_q][H][D]
@@ -122,12 +120,15 @@ struct PrefillArgs {
   int grouped;                      // grid order: query tiles of a (sequence, head) pair together
   int cus;                          // compute units of the device (0: unknown)
   float scale_log2;                 // |scale| * log2(e)
-  uint32_t q_sign;                  // 0x80008000 for a negative scale (queries negated), else 0
+  uint32_t q_sign;                  // negative scale (queries negated): 0x80008000, else 0
   int out_f32;
 };
 hipError_t launch_prefill_mfma(const PrefillArgs& a, Dt dt, int D, int BS, hipStream_t stream);
+hipError_t launch_prefill_f32(const PrefillArgs& a, int D, int BS, hipStream_t stream);
 int prefill_mfma_q_tile();
-// workgroups of the prefill kernel resident at once on each compute unit
+// workgroups of the prefill kernels (f16/bf16 standard shape; f32) resident
+// at once on each compute unit
 constexpr int kPrefillWorkgroupsPerCU = 3;
+constexpr int kPrefillF32WorkgroupsPerCU = 2;
 
 }  // namespace pa

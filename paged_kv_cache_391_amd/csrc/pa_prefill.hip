@@ -165,6 +165,74 @@ template <typename T> __device__ __forceinline__ uint32_t lds_offset(T* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)p;
 }
 
+// Work item of this workgroup: sequence s, head h, query tile qt (of QT
+// queries; key tiles of KTP keys price the items). False when the
+// workgroup has none (padding of the grouped grid).
+template <int KTP>
+__device__ __forceinline__ bool prefill_item(const PrefillArgs& a, int lane, int& s, int& h, int& qt) {
+  // Work order. With more workgroups than fit on the chip at once, the
+  // (sequence, head) pairs go in groups of 8: bid = x + 8 (qi + q_tiles grp),
+  // pair = 8 grp + x. Workgroups go round-robin over the 8 XCDs, so all
+  // query tiles of a pair land on one XCD one after another and walk the
+  // same keys together while the K/V tiles sit in that XCD's L2 (each K/V
+  // byte then leaves HBM about once instead of once per query tile).
+  // Otherwise every workgroup is resident at once; the (sequence, query
+  // tile) items are then taken heaviest first (priced from the lengths on
+  // the device), and the rounds in which the workgroups reach the compute
+  // units alternate direction, so heavy and light items share units.
+  if (a.grouped) {
+    const int x = blockIdx.x & 7;
+    const int rest = blockIdx.x >> 3;
+    const int pair = (rest / a.q_tiles) * 8 + x;
+    if (pair >= a.num_seqs * a.H) return false;
+    h = pair % a.H;
+    s = pair / a.H;
+    qt = a.q_tiles - 1 - rest % a.q_tiles;
+  } else {
+    // Workgroups are handed to compute units in order, one per unit per
+    // round (workgroup x, x + CUs, x + 2 CUs, ... share a unit). Every
+    // other round runs backwards, so the unit that holds one of the
+    // heaviest query tiles of the first round gets one of the lightest of
+    // the second.
+    int pos = blockIdx.x;
+    if (a.cus > 0) {
+      const int round = pos / a.cus, c = pos % a.cus;
+      if ((round & 1) && (round + 1) * a.cus <= (int)gridDim.x) pos = round * a.cus + (a.cus - 1 - c);
+    }
+    const int rank = pos / a.H;
+    h = pos % a.H;
+    const int n_items = a.num_seqs * a.q_tiles;
+    if (n_items <= 64) {
+      // Lane i prices work item i (sequence i / q_tiles, query tile
+      // i % q_tiles) at the key tiles its workgroup walks (0 when the chunk
+      // has no such query tile); the grid takes items by decreasing price,
+      // ties in index order, so the heaviest query tiles start first, one
+      // per compute unit. (More items than lanes: the fixed order, latest
+      // query tiles first.)
+      int price = -1;
+      if (lane < n_items) {
+        const int si = lane / a.q_tiles, qi = lane % a.q_tiles;
+        const ChunkRows r = chunk_rows(a.query_start_loc[si], a.query_start_loc[si + 1], a.context_lens[si],
+                                       a.total_q, a.max_context_len);
+        price = qi * QT < r.L ? (r.ctx - r.L + min((qi + 1) * QT, r.L) + KTP - 1) / KTP : 0;
+      }
+      int ahead = 0;  // items taken before item `lane`
+      for (int j = 0; j < n_items; ++j) {
+        const int pj = __builtin_amdgcn_readlane(price, j);
+        ahead += (pj > price || (pj == price && j < lane)) ? 1 : 0;
+      }
+      const uint64_t hit = __ballot(lane < n_items && ahead == rank);
+      const int item = hit ? (int)__builtin_ctzll(hit) : 0;  // exactly one lane holds each rank
+      s = item / a.q_tiles;
+      qt = item % a.q_tiles;
+    } else {
+      s = rank % a.num_seqs;
+      qt = a.q_tiles - 1 - rank / a.num_seqs;
+    }
+  }
+  return true;
+}
+
 }  // namespace
 
 template <Dt DT, int D, int BS, bool WIDE>
@@ -200,67 +268,8 @@ __global__ __launch_bounds__((PfShape<D, WIDE>::NW * 64))
   const int n16 = lane & 15;
   const int g4 = lane >> 4;
 
-  // Work order. With more workgroups than fit on the chip at once, the
-  // (sequence, head) pairs go in groups of 8: bid = x + 8 (qi + q_tiles grp),
-  // pair = 8 grp + x. Workgroups go round-robin over the 8 XCDs, so all
-  // query tiles of a pair land on one XCD one after another and walk the
-  // same keys together while the K/V tiles sit in that XCD's L2 (each K/V
-  // byte then leaves HBM about once instead of once per query tile).
-  // Otherwise every workgroup is resident at once; the (sequence, query
-  // tile) items are then taken heaviest first (priced from the lengths on
-  // the device), and the rounds in which the workgroups reach the compute
-  // units alternate direction, so heavy and light items share units.
   int h, s, qt;
-  if (a.grouped) {
-    const int x = blockIdx.x & 7;
-    const int rest = blockIdx.x >> 3;
-    const int pair = (rest / a.q_tiles) * 8 + x;
-    if (pair >= a.num_seqs * a.H) return;
-    h = pair % a.H;
-    s = pair / a.H;
-    qt = a.q_tiles - 1 - rest % a.q_tiles;
-  } else {
-    // Workgroups are handed to compute units in order, one per unit per
-    // round (workgroup x, x + CUs, x + 2 CUs, ... share a unit). Every
-    // other round runs backwards, so the unit that holds one of the
-    // heaviest query tiles of the first round gets one of the lightest of
-    // the second.
-    int pos = blockIdx.x;
-    if (a.cus > 0) {
-      const int round = pos / a.cus, c = pos % a.cus;
-      if ((round & 1) && (round + 1) * a.cus <= (int)gridDim.x) pos = round * a.cus + (a.cus - 1 - c);
-    }
-    const int rank = pos / a.H;
-    h = pos % a.H;
-    const int n_items = a.num_seqs * a.q_tiles;
-    if (n_items <= 64) {
-      // Lane i prices work item i (sequence i / q_tiles, query tile
-      // i % q_tiles) at the key tiles its workgroup walks (0 when the chunk
-      // has no such query tile); the grid takes items by decreasing price,
-      // ties in index order, so the heaviest query tiles start first, one
-      // per compute unit. (More items than lanes: the fixed order, latest
-      // query tiles first.)
-      int price = -1;
-      if (lane < n_items) {
-        const int si = lane / a.q_tiles, qi = lane % a.q_tiles;
-        const ChunkRows r = chunk_rows(a.query_start_loc[si], a.query_start_loc[si + 1], a.context_lens[si],
-                                       a.total_q, a.max_context_len);
-        price = qi * QT < r.L ? (r.ctx - r.L + min((qi + 1) * QT, r.L) + KT - 1) / KT : 0;
-      }
-      int ahead = 0;  // items taken before item `lane`
-      for (int j = 0; j < n_items; ++j) {
-        const int pj = __builtin_amdgcn_readlane(price, j);
-        ahead += (pj > price || (pj == price && j < lane)) ? 1 : 0;
-      }
-      const uint64_t hit = __ballot(lane < n_items && ahead == rank);
-      const int item = hit ? (int)__builtin_ctzll(hit) : 0;  // exactly one lane holds each rank
-      s = item / a.q_tiles;
-      qt = item % a.q_tiles;
-    } else {
-      s = rank % a.num_seqs;
-      qt = a.q_tiles - 1 - rank / a.num_seqs;
-    }
-  }
+  if (!prefill_item<KT>(a, lane, s, h, qt)) return;
   // lengths and row ranges clamped to what the host validated (in-range
   // values are unchanged): no read or write leaves the caller's buffers
   const ChunkRows cr =
@@ -582,6 +591,279 @@ __global__ __launch_bounds__((PfShape<D, WIDE>::NW * 64))
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// f32 causal prefill on the matrix cores. v_mfma_f32_16x16x4_f32 takes fp32
+// operands and accumulates in fp32 (no rounding of q, K, V or P), at the
+// chip's fp32 rate; what it adds over the vector ALUs is that each K/V tile
+// is staged in LDS once and shared by the workgroup's 128 queries (8 waves x
+// 16), instead of every query row walking its own causal prefix.
+// Same orientation as the f16/bf16 kernel: S^T = K Q^T, O^T += V^T P^T, with
+// the score accumulator a lane holds (query n16, keys 4 g4 + r) used as the
+// P^T operand of the k-steps that walk those keys, so P stays in registers
+// at full precision. Each MFMA contracts 4 values, so the operands are
+// read 4 k-steps at a time with one 16-byte LDS read per lane: Q.K steps
+// (t, u) take dims 16 t + 4 g4 + u, and the P.V product is cut into output
+// blocks (bb, u) whose row i is dim 64 bb + 4 i + u. A tile is 8 KiB of K
+// and 8 KiB of V (16 keys at head dim 128, 32 at 64), three tiles deep in
+// LDS by the LDS DMA; rows are XOR-swizzled by 16-byte chunk (chunk c of
+// row r at c ^ (r mod 16)), so both the K reads (16 rows, one chunk) and the
+// V reads (one row, 16 chunks) use every bank once.
+namespace {
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+}  // namespace
+
+template <int D, int BS>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void prefill_f32_kernel(const PrefillArgs a) {
+  constexpr int NW = 8;              // waves per workgroup, 16 queries each
+  constexpr int KTF = 2048 / D;      // keys per tile: 8 KiB of K and of V
+  constexpr int NSUB = KTF / 16;     // 16-key subtiles
+  constexpr int NT = D / 16;         // groups of 4 Q.K k-steps (16 dims)
+  constexpr int NBB = D / 64;        // 64-dim blocks of O^T (4 MFMA outputs each)
+  constexpr int NCH = 4;             // Q.K accumulation chains
+  constexpr int CPR = D / 4;         // 16-byte chunks per row
+  constexpr int ROWB = D * 4;        // bytes per K/V row
+  constexpr int TILEB = KTF * ROWB;  // 8 KiB
+  constexpr int PR = 1024 / ROWB;    // rows per 1 KiB DMA piece (one per wave)
+  static_assert(TILEB == 1024 * NW && CPR >= 16, "one DMA piece per wave; rows of at least 16 chunks");
+  static_assert(PR <= BS && BS % PR == 0, "the rows of one DMA piece lie in one block");
+  static_assert(NW * 16 == QT, "the query tile of the f16/bf16 kernel");
+
+  __shared__ __align__(1024) uint8_t sk[NBUF][TILEB];
+  __shared__ __align__(1024) uint8_t sv[NBUF][TILEB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n16 = lane & 15;
+  const int g4 = lane >> 4;
+
+  int h, s, qt;
+  if (!prefill_item<KTF>(a, lane, s, h, qt)) return;
+  const ChunkRows cr =
+      chunk_rows(a.query_start_loc[s], a.query_start_loc[s + 1], a.context_lens[s], a.total_q, a.max_context_len);
+  const int ctx = cr.ctx, q_beg = cr.q_beg, L = cr.L;
+  const int j0 = qt * QT;
+  if (j0 >= L) return;
+  const int c0 = ctx - L;                          // position of the chunk's first query
+  const int kv_end = c0 + min(j0 + QT, L);         // keys this workgroup needs: [0, kv_end)
+  const int n_tiles = (kv_end + KTF - 1) / KTF;
+  const int wq0 = j0 + wave * 16;                  // the wave's first query (chunk-relative)
+  const bool wave_active = wq0 < L;
+  const int wave_last_pos = c0 + min(wq0 + 16, L) - 1;
+
+  const char* kc = reinterpret_cast<const char*>(a.k_cache);
+  const char* vc = reinterpret_cast<const char*>(a.v_cache);
+  const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks;
+  const int nb = (kv_end + BS - 1) / BS;           // blocks this workgroup reads
+  const uint32_t blk_bytes = (uint32_t)a.H * BS * ROWB;   // one block of every head (< 2^32)
+  const uint32_t head_bytes = (uint32_t)h * BS * ROWB;
+
+  // Q^T operand of k-step (t, u): query n16, dim 16 t + 4 g4 + u
+  const int jq = wq0 + n16;
+  const uint32_t qsign = a.q_sign ? 0x80000000u : 0u;
+  f32x4 qf[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (jq < L) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(a.q) +
+                                                       ((int64_t)(q_beg + jq) * a.H + h) * D + 16 * t + 4 * g4);
+      qf[t] = __builtin_bit_cast(f32x4, u32x4{v[0] ^ qsign, v[1] ^ qsign, v[2] ^ qsign, v[3] ^ qsign});
+    } else {
+      qf[t] = zero4();
+    }
+  }
+  // o[bb][u]: O^T rows d = 64 bb + 4 i + u (i = 4 g4 + r), query n16;
+  // lsum: this lane's share of the softmax denominator (its keys' P)
+  f32x4 o[NBB][4];
+#pragma unroll
+  for (int bb = 0; bb < NBB; ++bb)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) o[bb][u] = zero4();
+  float m = -INFINITY, lsum = 0.f;
+
+  // DMA: wave w moves rows w*PR .. w*PR+PR-1 of each tile; lane L fills
+  // chunk position L % CPR of row L / CPR from source chunk (L % CPR) ^ sw
+  const int prow = lane / CPR;
+  const int pcol = lane % CPR;
+  const uint32_t src = prow * ROWB + ((pcol ^ ((wave * PR + prow) & 15)) * 16);
+  const uint32_t sk0 = lds_offset(&sk[0][0]);
+  const uint32_t sv0 = lds_offset(&sv[0][0]);
+  auto entry = [&](int t) {
+    const uint32_t k = (uint32_t)(t * KTF + wave * PR);
+    return bt_row + min(k / BS, (uint32_t)(nb - 1));
+  };
+  auto dma_id = [&](int t, int b, int phys) {
+    const uint32_t key = (uint32_t)(t * KTF + wave * PR);
+    const uint64_t row = (uint64_t)(uint32_t)clamp_block(phys, a.num_blocks) * blk_bytes + (head_bytes + (key % BS) * ROWB);
+    lds_dma16s(kc + row, src, sk0 + b * TILEB + wave * 1024);
+    lds_dma16s(vc + row, src, sv0 + b * TILEB + wave * 1024);
+  };
+  auto zero_tail = [&](int t, int b) {
+    const int r0 = kv_end - t * KTF;
+    for (int i = tid; i < (KTF - r0) * CPR; i += NW * 64)
+      *reinterpret_cast<u32x4*>(&sv[b][(r0 + i / CPR) * ROWB + (i % CPR) * 16]) = u32x4{0u, 0u, 0u, 0u};
+  };
+  // LDS offsets of the operand reads: K row 16 sub + n16, chunk 4 t + g4;
+  // V row 16 sub + 4 g4 + j, chunk 16 bb + n16 (the swizzle of both rows is
+  // their row index mod 16: n16, and 4 g4 + j)
+  const uint32_t k_rd = n16 * ROWB + ((g4 ^ n16) * 16);  // t enters as an XOR of 4 t into the chunk index
+  const float c = fmaxf(a.scale_log2, 1.17549435e-38f);
+
+  auto compute = [&](auto bc, int kv0) {
+    constexpr int b = decltype(bc)::value;
+    // Four independent accumulation chains over the dims (k-step (t, u) goes
+    // to chain u), added pairwise at the end: fp32 chains of a quarter of the
+    // steps over smaller partial sums round about as little as a per-lane
+    // dot product finished by a butterfly (a single chain's rounding error
+    // of the scores, amplified by the exponent at large scales, would exceed
+    // 1e-5 on the outputs), and consecutive MFMAs do not wait on each other
+    f32x4 sacc[NSUB];
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) {
+      f32x4 ch[NCH];
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) ch[i] = zero4();
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const f32x4 ka = *reinterpret_cast<const f32x4*>(&sk[b][sub * 16 * ROWB + (k_rd ^ (t << 6))]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ch[u % NCH] = mfma4(ka[u], qf[t][u], ch[u % NCH]);
+      }
+#pragma unroll
+      for (int w = NCH / 2; w >= 1; w /= 2)
+#pragma unroll
+        for (int i = 0; i < w; ++i) ch[i] += ch[i + w];
+      sacc[sub] = ch[0];
+    }
+    if (kv0 + KTF - 1 > c0 + wq0) {  // keys past a query's position score -inf
+      const int last_key = min(c0 + jq, kv_end - 1);
+#pragma unroll
+      for (int sub = 0; sub < NSUB; ++sub)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (kv0 + 16 * sub + 4 * g4 + r > last_key) sacc[sub][r] = -INFINITY;
+    }
+    // online softmax with the lazy max of the f16/bf16 kernel
+    float mr = -INFINITY;
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mr = fmaxf(mr, sacc[sub][r]);
+    if (__any(mr * c > m + RESCALE_LOG2)) {
+      const float mt = rows4_max(mr) * c;
+      const bool grow = mt > m + RESCALE_LOG2;
+      if (__any(grow)) {
+        const float m_new = grow ? mt : m;
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        lsum *= alpha;
+#pragma unroll
+        for (int bb = 0; bb < NBB; ++bb)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) o[bb][u] *= alpha;
+        m = m_new;
+      }
+    }
+    const float neg_m = m == -INFINITY ? 0.f : -m;
+    f32x4 p[NSUB];
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[sub][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[sub][r], c, neg_m));
+        lsum += p[sub][r];
+      }
+    // O^T += V^T P^T: k-step (sub, j) takes keys 16 sub + 4 k + j, whose P
+    // lane (k, n16) already holds in p[sub][j]
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int bb = 0; bb < NBB; ++bb) {
+          const int vr = 16 * sub + 4 * g4 + j;
+          const f32x4 va = *reinterpret_cast<const f32x4*>(
+              &sv[b][vr * ROWB + (((16 * bb + n16) ^ (4 * g4 + j)) * 16)]);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) o[bb][u] = mfma4(va[u], p[sub][j], o[bb][u]);
+        }
+  };
+
+  // The pipeline of the f16/bf16 kernel with one DMA piece per wave: tile
+  // t+2 in flight while tile t is computed; one barrier per tile. The Q
+  // loads complete before the first DMA, so no wait inside the loop drains
+  // the DMA queue for them.
+#pragma unroll
+  for (int t = 0; t < NT; ++t) asm volatile("" : "+v"(qf[t]));
+  const int last = n_tiles - 1;
+  {
+    int ida, idb;
+    sload2(entry(0), entry(min(1, last)), ida, idb);
+    dma_id(0, 0, ida);
+    dma_id(min(1, last), 1, idb);
+  }
+  static_assert(NBUF == 3, "three LDS buffers");
+  auto iter = [&](int t, auto bc) {
+    constexpr int b = decltype(bc)::value;
+    const int tn = min(t + NBUF - 1, last);
+    const int32_t* e[1] = {entry(tn)};
+    int ids[1];
+    sload_barrier<1, 2 * (NBUF - 2)>(e, ids);
+    if ((t + 1) * KTF > kv_end) {
+      zero_tail(t, b);
+      __syncthreads();
+    }
+    dma_id(tn, (b + NBUF - 1) % NBUF, ids[0]);
+    if (wave_active && t * KTF <= wave_last_pos) compute(bc, t * KTF);
+  };
+  for (int t = 0; t < n_tiles; t += NBUF)
+    for_each_const(
+        [&](auto bc) {
+          if (t + decltype(bc)::value < n_tiles) iter(t + decltype(bc)::value, bc);
+        },
+        std::make_integer_sequence<int, NBUF>{});
+  wait_vmcnt0();  // no DMA may still be writing this workgroup's LDS when it ends
+
+  if (!wave_active) return;
+  const float l2 = lsum + __shfl_xor(lsum, 16);
+  const float lt = l2 + __shfl_xor(l2, 32);
+  if (jq >= L) return;
+  float* orow = reinterpret_cast<float*>(a.out) + ((int64_t)(q_beg + jq) * a.H + h) * D;
+#pragma unroll
+  for (int bb = 0; bb < NBB; ++bb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      *reinterpret_cast<f32x4*>(orow + 64 * bb + 16 * g4 + 4 * r) =
+          f32x4{o[bb][0][r] / lt, o[bb][1][r] / lt, o[bb][2][r] / lt, o[bb][3][r] / lt};
+}
+
+template <int D, int BS>
+static hipError_t launch_f32(const PrefillArgs& a, hipStream_t stream) {
+  const int64_t pairs = (int64_t)a.num_seqs * a.H;
+  const int64_t grid = (int64_t)a.q_tiles * (a.grouped ? (pairs + 7) / 8 * 8 : pairs);
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((prefill_f32_kernel<D, BS>), dim3((unsigned)grid), dim3(512), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t dispatch_f32_bs(const PrefillArgs& a, int BS, hipStream_t stream) {
+  switch (BS) {
+    case 8: return launch_f32<D, 8>(a, stream);
+    case 16: return launch_f32<D, 16>(a, stream);
+    case 32: return launch_f32<D, 32>(a, stream);
+    case 64: return launch_f32<D, 64>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_f32(const PrefillArgs& a, int D, int BS, hipStream_t stream) {
+  if (D == 128) return dispatch_f32_bs<128>(a, BS, stream);
+  if (D == 64) return dispatch_f32_bs<64>(a, BS, stream);
+  return hipErrorInvalidValue;
 }
 
 int prefill_mfma_q_tile() { return QT; }

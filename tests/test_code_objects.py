@@ -55,7 +55,11 @@ def _kernels(tmp_path):
 
 def test_no_kernel_uses_scratch(tmp_path):
     ks = _kernels(tmp_path)
-    assert len(ks) >= 90, "expected every instantiation of every kernel"
+    # decode partitions 3 dtypes x 2 head dims x 4 block sizes (24), f16/bf16
+    # prefill 2 x 2 x 4 + its wide shape 2 x 4 (24), f32 prefill 2 x 4 (8),
+    # shared-prefix step 2 x 2 x 4 (16), reductions 3 x 2 x 2 (12), cache
+    # write, block copy, gather (3)
+    assert len(ks) >= 87, "expected every instantiation of every kernel"
     bad = {n: m for n, m in ks.items()
            if m["vgpr_spill_count"] or m["sgpr_spill_count"] or m["private_segment_fixed_size"]}
     assert not bad, f"kernels spilling to scratch: {sorted(bad)[:5]}"

@@ -556,7 +556,7 @@ def test_prefill_empty_chunks_between_others(dtype):
     assert np.abs(got - ref).max() <= ATOL[dtype]
 
 
-@pytest.mark.parametrize("dtype,bs", [("f16", 8), ("bf16", 16), ("f16", 64)])
+@pytest.mark.parametrize("dtype,bs", [("f16", 8), ("bf16", 16), ("f16", 64), ("f32", 8), ("f32", 64)])
 def test_prefill_head_dim_64(dtype, bs):
     """head_dim 64: a wave's V rows of one load span two 8-token blocks at
     block size 8 (the kernel's per-lane block choice)."""
@@ -573,7 +573,7 @@ def test_prefill_head_dim_64(dtype, bs):
     assert err <= ATOL[dtype], f"prefill max abs err {err:.3e}"
 
 
-@pytest.mark.parametrize("dtype,bs", [("f16", 8), ("bf16", 16), ("f16", 32), ("bf16", 64)])
+@pytest.mark.parametrize("dtype,bs", [("f16", 8), ("bf16", 16), ("f16", 32), ("bf16", 64), ("f32", 8), ("f32", 16)])
 def test_prefill_tile_aligned_contexts(dtype, bs):
     """Contexts and chunk starts on multiples of the 32-key tile: the last key
     tile is full (no rows past the context to clear), and query tiles start
@@ -594,7 +594,7 @@ def test_prefill_tile_aligned_contexts(dtype, bs):
     assert err <= ATOL[dtype], f"prefill max abs err {err:.3e}"
 
 
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("scale", [-0.2, 0.0])
 def test_prefill_negative_and_zero_scale(dtype, scale):
     """A negative scale (run as |scale| on sign-flipped queries) and a zero
@@ -613,7 +613,7 @@ def test_prefill_negative_and_zero_scale(dtype, scale):
     assert err <= ATOL[dtype], f"prefill max abs err {err:.3e}"
 
 
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("scale", [None, 1.0])
 def test_prefill_long_context_and_wide_scores(dtype, scale):
     """Contexts of hundreds of blocks (block ids read far into the table row)
@@ -634,7 +634,7 @@ def test_prefill_long_context_and_wide_scores(dtype, scale):
 
 
 @pytest.mark.parametrize("dtype,D,bs", [("f16", 128, 16), ("bf16", 128, 16), ("f16", 64, 32), ("bf16", 128, 64),
-                                        ("f16", 128, 8)])
+                                        ("f16", 128, 8), ("f32", 128, 16), ("f32", 64, 8)])
 def test_prefill_many_workgroups_grouped_order(dtype, D, bs):
     """More query tiles than the chip holds at once (15 chunks x 13 heads x 4
     tiles of 128 queries = 780 workgroups, more than 3 per compute unit): the
@@ -690,6 +690,24 @@ def test_prefill_bench_workload_full_output():
     assert err <= ATOL[wl.dtype]
     outn = od.prefill(TORCH_DT[wl.dtype])
     assert np.array_equal(bits(host(outn)), bits(rne(out32, wl.dtype)))
+
+
+def test_prefill_f32_bench_workload_full_output():
+    """bench.py's f32 prefill (the mixed step's 4 chunks with f32 caches,
+    40 heads x 128, 640 workgroups) in the launch configuration it times:
+    every output element against the oracle."""
+    import bench
+    wl = bench.prefill_config("prefill_f32")
+    od = _on_device_written(wl)
+    p = wl.prefill
+    kc, vc = oracle.reshape_and_cache(wl.new.k, wl.new.v, wl.k_cache, wl.v_cache, wl.new.slot_mapping,
+                                      wl.block_size, wl.dtype)
+    out32 = host(od.prefill(torch.float32))
+    assert np.isfinite(out32).all()
+    ref = oracle.prefill(p.q, kc, vc, p.block_tables, p.context_lens, p.query_start_loc, wl.scale, wl.dtype)
+    err = np.abs(out32.astype(np.float64) - ref).max()
+    print(f"prefill_f32 max abs err {err:.3e}")
+    assert err <= ATOL[wl.dtype]
 
 
 def test_prefill_config5_full_output():
