@@ -22,9 +22,8 @@ Other workloads (``--workload``), same machinery:
               1536 cached tokens (150 GFLOP): the compute-bound path, reported
               in TFLOP/s against the dense MFMA peak
   prefill_f32 the mixed step's cache write and its 4 prefill chunks with f32
-              caches and queries: the f32 prefill, one decode wave per query
-              row (each row re-reads its causal prefix), in TFLOP/s against
-              the fp32 vector peak
+              caches and queries: the f32 prefill kernel, in TFLOP/s against
+              the dense fp32 MFMA peak
 
 One step = the workload's whole path, all inputs resident in HBM:
 reshape_and_cache of the step's new tokens, [prefill,] then split-K decode
@@ -57,9 +56,8 @@ if ROOT not in sys.path:
 METRIC = "paged decode attention achieved HBM GB/s (% of peak) at LLaMA-7B layer shape"
 METRIC_OTHER = "paged attention step achieved HBM GB/s (% of peak)"
 HBM_PEAK_GBPS = 8000.0
-MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # dense fp16/bf16 matrix-core peak of MI355X
-# fp32 vector peak: 256 CUs x 4 SIMDs x 16 lanes x 2 (FMA) x 2 (packed FP32) x 2.4 GHz
-F32_VALU_PEAK_TFLOPS = 157.3
+# dense matrix-core peaks of MI355X (fp32 equals the fp32 vector rate)
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
 PREFILL_WORKLOADS = ("prefill_long", "prefill_f32")
 KERNEL_SOURCES = ["pa_decode.hip", "pa_decode_device.h", "pa_device.h", "pa_bounds.h", "pa_internal.h"]
 SHARED_KERNEL_SOURCES = KERNEL_SOURCES + ["pa_shared.hip"]
@@ -84,7 +82,7 @@ WORKLOADS = {
                    "(L U[256,512], prior U[0,1024]), 40 heads x 128, f32, block_size 16, seed 396",
 }
 PREFILL_METRIC = "causal paged prefill achieved TFLOP/s (% of the dense MFMA peak)"
-PREFILL_F32_METRIC = "causal paged prefill achieved TFLOP/s (% of the fp32 vector peak)"
+PREFILL_F32_METRIC = "causal paged prefill achieved TFLOP/s (% of the dense fp32 MFMA peak)"
 
 
 def traffic_file(workload, shared=False):
@@ -100,12 +98,14 @@ def traffic_kernel(shared, workload=None):
     kernel for the compute-bound workload."""
     if workload == "prefill_long":
         return "prefill_mfma_kernel"
+    if workload == "prefill_f32":
+        return "prefill_f32_kernel"
     return "shared_prefix_step_kernel" if shared else "decode_partition_kernel"
 
 
 def kernel_source_hash(shared=False, workload=None):
     h = hashlib.sha256()
-    names = PREFILL_KERNEL_SOURCES if workload == "prefill_long" else (
+    names = PREFILL_KERNEL_SOURCES if workload in PREFILL_WORKLOADS else (
         SHARED_KERNEL_SOURCES if shared else KERNEL_SOURCES)
     for name in names:
         with open(os.path.join(ROOT, "paged_kv_cache_391_amd", "csrc", name), "rb") as f:
@@ -430,7 +430,7 @@ def prefill_main(args):
             raise SystemExit("graph replay disagrees with the eager step")
 
     f32 = wl.dtype == "f32"
-    peak = F32_VALU_PEAK_TFLOPS if f32 else MFMA_PEAK_TFLOPS[wl.dtype]
+    peak = MFMA_PEAK_TFLOPS[wl.dtype]
     cold_ms = float(cold_pf.mean())
     pf_tflops = flops / (cold_ms * 1e-3) / 1e12
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -486,9 +486,9 @@ def prefill_main(args):
         "config": {"workload": WORKLOADS[args.workload], "global_batch": int(p.num_seqs),
                    "seq_len": int(p.max_context_len), "parallelism": "none (1 GPU)"},
         "pct_of_peak": round(100 * value / peak, 2),
-        "roofline": {"bound": "alu" if f32 else "mfma", "achieved": round(pf_tflops, 1), "peak": peak,
+        "roofline": {"bound": "mfma", "achieved": round(pf_tflops, 1), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(pf_tflops / peak, 4), "traffic": traffic,
-                     "kernel": (f"decode_partition_kernel<f32,{D},{wl.block_size},PrefillRows>" if f32 else
+                     "kernel": (f"prefill_f32_kernel<{D},{wl.block_size}>" if f32 else
                                 f"prefill_mfma_kernel<{wl.dtype},{D},{wl.block_size}>"),
                      "flops_per_launch": flops, "bytes_per_launch": pf_bytes,
                      "avg_launch_us": round(cold_ms * 1e3, 2),
@@ -498,9 +498,6 @@ def prefill_main(args):
                      "launch_us": pct(cold_pf), "warm_avg_launch_us": round(pf_ms * 1e3, 2),
                      "hbm_frac": round(pf_bytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                      "roofline_us": round(max(flops / (peak * 1e12), pf_bytes / (HBM_PEAK_GBPS * 1e9)) * 1e6, 2)},
-        # f32: each query row is its own decode over its causal prefix, so the
-        # K/V bytes it reads grow with L x ctx instead of ctx
-        "row_path_kv_bytes": (flops // (4 * D)) * D * elt * 2 if f32 else None,
         "timing": "hip_graph_replay" if not args.eager else "eager",
         "eager_ms_per_step": round(eager_ms, 5),
         "hbm_copy_probe_GBps": round(copy_gbps, 1),

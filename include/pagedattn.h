@@ -345,8 +345,9 @@ pa_status pa_paged_attention_decode_shared_prefix(
  *   query_start_loc  int32 [num_seqs+1], query_start_loc[0] == 0,
  *                    query_start_loc[num_seqs] == total_q
  *   max_q_len        >= every L_s (sizes the grid)
- * f16/bf16 run on matrix cores (MFMA, fp32 accumulate, P rounded to the
- * input dtype before the P.V product); f32 runs on the vector path.
+ * All dtypes run on matrix cores with fp32 accumulation: f16/bf16 round P
+ * to the input dtype before the P.V product; f32 keeps every operand in
+ * fp32.
  * Preconditions: non-decreasing query_start_loc, L_s <= context_lens[s] <=
  * max_context_len <= max_blocks_per_seq * block_size, valid table entries.
  * Errors: INVALID_ARG, UNSUPPORTED, HIP.
