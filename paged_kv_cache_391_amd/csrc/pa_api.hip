@@ -452,6 +452,7 @@ static pa_status prepare_prefill(PrefillCall& call, void* out, pa_dtype out_dtyp
   a.cus = cus;
   const int per_cu = dtype == PA_F32 ? pa::kPrefillF32WorkgroupsPerCU : pa::kPrefillWorkgroupsPerCU;
   a.grouped = cus > 0 && (int64_t)a.q_tiles * num_heads * num_seqs > (int64_t)cus * per_cu;
+  a.wide = !a.grouped;  // every workgroup resident at once
   return PA_OK;
 }
 
@@ -515,7 +516,10 @@ pa_status pa_attention_step(const pa_step_args* s, hipStream_t stream, hipStream
   if (e != hipSuccess) return hip_status(e);
   if (fork) {
     // the prefill runs on the side stream next to the decode: both only read
-    // the cache the write above produced
+    // the cache the write above produced. Next to the decode's waves the
+    // prefill's 4-wave workgroups find room sooner than 8-wave ones (the
+    // mixed step: 742 against 772 us), so it keeps its standard shape.
+    pf.pf.wide = 0;
     e = hipEventRecord(fork_event, stream);
     if (e == hipSuccess) e = hipStreamWaitEvent(side_stream, fork_event, 0);
     if (e == hipSuccess) e = launch_prefill(pf, side_stream);

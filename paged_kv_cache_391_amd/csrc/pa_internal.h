@@ -118,6 +118,7 @@ struct PrefillArgs {
   int num_blocks;
   int q_tiles;                      // grid: q tiles per sequence
   int grouped;                      // grid order: query tiles of a (sequence, head) pair together
+  int wide;                         // f16/bf16, head dim 128: the wide workgroup shape
   int cus;                          // compute units of the device (0: unknown)
   float scale_log2;                 // |scale| * log2(e)
   uint32_t q_sign;                  // negative scale (queries negated): 0x80008000, else 0

@@ -875,7 +875,7 @@ static hipError_t launch_k4(const PrefillArgs& a, hipStream_t stream) {
   if (grid == 0) return hipSuccess;
   // every workgroup resident at once: the wide shape (head dim 128)
   if constexpr (D == 128) {
-    if (!a.grouped) {
+    if (a.wide) {
       hipLaunchKernelGGL((prefill_mfma_kernel<DT, D, BS, true>), dim3((unsigned)grid), dim3(PfShape<D, true>::NW * 64),
                          0, stream, a);
       return hipGetLastError();
