@@ -20,23 +20,23 @@ pytestmark = pytest.mark.gpu
 
 
 @functools.lru_cache(maxsize=None)
-def _config(cid):
-    wl = make_config(cid)
+def _config(cid, dtype=None):
+    wl = make_config(cid) if dtype is None else make_config(cid, dtype=dtype)
     kc, vc = oracle.reshape_and_cache(wl.new.k, wl.new.v, wl.k_cache, wl.v_cache, wl.new.slot_mapping,
                                       wl.block_size, wl.dtype)
     return wl, kc, vc
 
 
 @functools.lru_cache(maxsize=None)
-def _oracle_decode(cid):
-    wl, kc, vc = _config(cid)
+def _oracle_decode(cid, dtype=None):
+    wl, kc, vc = _config(cid, dtype)
     d = wl.decode
     return oracle.decode(d.q, kc, vc, d.block_tables, d.context_lens, wl.scale, wl.dtype)
 
 
 @functools.lru_cache(maxsize=None)
-def _oracle_prefill(cid):
-    wl, kc, vc = _config(cid)
+def _oracle_prefill(cid, dtype=None):
+    wl, kc, vc = _config(cid, dtype)
     p = wl.prefill
     return oracle.prefill(p.q, kc, vc, p.block_tables, p.context_lens, p.query_start_loc, wl.scale, wl.dtype)
 
@@ -787,14 +787,16 @@ def test_mixed_step_graph_replays_match_eager():
         assert torch.isfinite(extra).all()
 
 
-@pytest.mark.parametrize("side", [False, True])
-def test_attention_step_matches_the_separate_calls(side):
+@pytest.mark.parametrize("side,dtype", [(False, None), (True, None), (True, "f32")])
+def test_attention_step_matches_the_separate_calls(side, dtype):
     """One scheduler iteration in one call (cache write, prefill, decode),
-    in order on one stream or with the prefill on a side stream: both fp32
-    outputs within tolerance of the oracle on every element, outputs and
-    caches equal, bit for bit, those of the three separate calls; captured
-    as a graph (fork/join across the two streams), every replay too."""
-    wl, _, _ = _config(5)
+    in order on one stream or with the prefill on a side stream (and with
+    f32 caches): both fp32 outputs within tolerance of the oracle on every
+    element, outputs and caches equal, bit for bit, those of the three
+    separate calls; captured as a graph (fork/join across the two streams),
+    every replay too."""
+    args = (5,) if dtype is None else (5, dtype)  # the same cache entries as the other tests
+    wl, _, _ = _config(*args)
     d, p = wl.decode, wl.prefill
     ref = OnDevice(wl)
     ws = pa.make_decode_workspace(d.num_seqs, wl.num_heads, wl.head_dim, d.max_context_len)
@@ -827,8 +829,8 @@ def test_attention_step_matches_the_separate_calls(side):
     torch.cuda.synchronize()
     assert torch.equal(pout, pref) and torch.equal(dout, dref)
     # and the step's own outputs against the oracle, element by element
-    _check_attention(pout, _oracle_prefill(5), wl.dtype)
-    _check_attention(dout, _oracle_decode(5), wl.dtype)
+    _check_attention(pout, _oracle_prefill(*args), wl.dtype)
+    _check_attention(dout, _oracle_decode(*args), wl.dtype)
     # unused slots hold NaN poison: compare the caches' bits
     assert np.array_equal(bits(host(od.k_cache)), bits(host(ref.k_cache)))
     assert np.array_equal(bits(host(od.v_cache)), bits(host(ref.v_cache)))
