@@ -171,9 +171,34 @@ __device__ __forceinline__ int group_prefix(const DecodeArgs& a, int g) {
   const int r1 = min(max(a.group_starts[g + 1], r0), a.num_rows);
   int p = a.prefix_lens[g];
   for (int r = r0 + lane; r < r1; r += 64) p = min(p, row_ctx(a, r));
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) p = min(p, __shfl_xor(p, s));
-  return max(p, 0) & ~15;
+  return max(wave_min_i(p), 0) & ~15;
+}
+
+// group_prefix(a, group_of_row(...)) for row r in a single dependent
+// memory round trip when there are at most 63 groups: lane i reads
+// group_starts[i], prefix_lens[i] and the length of row r - 31 + i at once,
+// so the group's start, end and requested prefix come out of registers once
+// the ballot has found the group, and so do the members' lengths whenever
+// the group lies within those 64 rows (always for groups of up to 32 rows);
+// otherwise they are read after it. Same result as the general path.
+// Called by whole waves (every lane active).
+__device__ __forceinline__ int row_group_prefix(const DecodeArgs& a, int r) {
+  if (a.num_groups < 1 || a.num_groups > 63) return group_prefix(a, group_of_row(a.group_starts, a.num_groups, r));
+  const int lane = __lane_id();
+  const int gs = a.group_starts[min(lane, a.num_groups)];
+  const int pl = a.prefix_lens[min(lane, a.num_groups - 1)];
+  const int w = r - 31 + lane;  // a window of rows around r
+  const int cw = w >= 0 && w < a.num_rows ? row_ctx(a, w) : 0;
+  const int g = __popcll(__ballot(lane >= 1 && lane < a.num_groups && gs <= r));
+  const int r0 = min(max(__builtin_amdgcn_readlane(gs, g), 0), a.num_rows);
+  const int r1 = min(max(__builtin_amdgcn_readlane(gs, g + 1), r0), a.num_rows);
+  int p = __builtin_amdgcn_readlane(pl, g);
+  if (r0 >= r - 31 && r1 <= r + 33) {
+    if (w >= r0 && w < r1) p = min(p, cw);
+  } else {
+    for (int m = r0 + lane; m < r1; m += 64) p = min(p, row_ctx(a, m));
+  }
+  return max(wave_min_i(p), 0) & ~15;
 }
 
 // Partition layout of one row: own partitions cover tokens [tok0, ctx) in
@@ -188,7 +213,7 @@ template <RowMode MODE>
 __device__ __forceinline__ RowParts row_parts(const DecodeArgs& a, int row, int ctx) {
   RowParts rp{0, 0, 0};
   if constexpr (MODE == RowMode::SharedTail) {
-    const int p = group_prefix(a, group_of_row(a.group_starts, a.num_groups, row));
+    const int p = row_group_prefix(a, row);
     const int pt = a.shared_part_tiles * 16;
     rp.tok0 = p;
     rp.poff = (p + pt - 1) / pt;

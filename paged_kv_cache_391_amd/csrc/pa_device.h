@@ -142,6 +142,20 @@ __device__ __forceinline__ float rows4_sum(float x) {
   return __builtin_bit_cast(float, (int)b[0]) + __builtin_bit_cast(float, (int)b[1]);
 }
 
+// Min of an int over the whole wave, every lane receiving it: DPP steps
+// within each 16-lane row (as row16_sum), then the row-swap instructions
+// across rows. VALU only. Every lane must be active.
+__device__ __forceinline__ int wave_min_i(int x) {
+  x = min(x, __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xf, 0xf, false));   // quad_perm(1,0,3,2)
+  x = min(x, __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xf, 0xf, false));   // quad_perm(2,3,0,1)
+  x = min(x, __builtin_amdgcn_update_dpp(0, x, 0x141, 0xf, 0xf, false));  // row_half_mirror
+  x = min(x, __builtin_amdgcn_update_dpp(0, x, 0x140, 0xf, 0xf, false));  // row_mirror
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = min((int)a[0], (int)a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return min((int)b[0], (int)b[1]);
+}
+
 // xor shuffle across the whole wave (through ds_bpermute)
 __device__ __forceinline__ float shfl_xor_f(float x, int m) {
   int lane = __lane_id();

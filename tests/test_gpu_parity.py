@@ -496,12 +496,15 @@ def test_shared_prefix_decode_ragged_groups(dtype, bs):
     assert torch.equal(out, again)
 
 
-def test_shared_prefix_decode_more_groups_than_a_wave_has_lanes():
-    """70 prefix-sharing groups: a row finds its group by counting the group
-    starts at or before it, 64 starts per ballot, so this takes two."""
-    rng = np.random.default_rng(70)
+@pytest.mark.parametrize("n_groups", [63, 70])
+def test_shared_prefix_decode_more_groups_than_a_wave_has_lanes(n_groups):
+    """63 prefix-sharing groups (the most whose starts and prefixes one wave
+    reads in a single load per lane) and 70: a row then finds its group by
+    counting the group starts at or before it, 64 starts per ballot, so
+    this takes two."""
+    rng = np.random.default_rng(n_groups)
     groups = []
-    for i in range(70):
+    for i in range(n_groups):
         n = 1 + i % 3
         groups.append((n, 16 * (i % 5), [int(t) for t in rng.integers(0, 40, n)]))
     kc, vc, q, bt, ctx, gs, pl = _grouped_batch("f16", 16, groups, 77)
