@@ -75,7 +75,8 @@ __global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_kernel(const 
   // partition p's (m, l) and the first PRE partitions' accumulators are read
   // at once (indices clamped to the row's partitions, weights zero past
   // them), so the merge waits on memory about once instead of once per
-  // partition. M and L are butterfly reductions across the wave; the
+  // partition. M and L are reductions across the wave (DPP and row-swap
+  // instructions, no LDS round trip); the
   // weighted sum of the accumulators runs in partition order.
   constexpr int PRE = 8;
   float xa[PRE][PER];
@@ -88,13 +89,11 @@ __global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_kernel(const 
   const float l_l = ml[2 * pl + 1];
   float M = lane < nparts ? m_l : -INFINITY;
   for (int p = lane + 64; p < nparts; p += 64) M = fmaxf(M, ml[2 * p]);
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) M = fmaxf(M, shfl_xor_f(M, s));
+  M = wave_max_f(M);
   const float w_l = lane < nparts ? fast_exp2(m_l - M) : 0.f;  // weight of partition `lane`
   float Lsum = l_l * w_l;
   for (int p = lane + 64; p < nparts; p += 64) Lsum += ml[2 * p + 1] * fast_exp2(ml[2 * p] - M);
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) Lsum += shfl_xor_f(Lsum, s);
+  Lsum = wave_sum_f(Lsum);
   float x[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) x[i] = 0.f;

@@ -332,22 +332,14 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int b
     }
   }
 
-  // merge the four 16-lane rows of the wave (same lane column c)
-  float m_all = fmaxf(st.m, shfl_xor_f(st.m, 16));
-  m_all = fmaxf(m_all, shfl_xor_f(m_all, 32));
+  // merge the four 16-lane rows of the wave (same lane column c) with the
+  // row-swap instructions (VALU, no LDS round trip)
+  const float m_all = rows4_max(st.m);
   {
     const float f = fast_exp2(st.m - (m_all == -INFINITY ? 0.f : m_all));
-    float lw = st.l * f;
-    lw += shfl_xor_f(lw, 16);
-    lw += shfl_xor_f(lw, 32);
-    st.l = lw;
+    st.l = rows4_sum(st.l * f);
 #pragma unroll
-    for (int k = 0; k < L::EPL; ++k) {
-      float x = st.acc[k] * f;
-      x += shfl_xor_f(x, 16);
-      x += shfl_xor_f(x, 32);
-      st.acc[k] = x;
-    }
+    for (int k = 0; k < L::EPL; ++k) st.acc[k] = rows4_sum(st.acc[k] * f);
     st.m = m_all;
   }
   if (g != 0) return;

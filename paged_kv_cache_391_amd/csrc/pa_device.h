@@ -142,6 +142,17 @@ __device__ __forceinline__ float rows4_sum(float x) {
   return __builtin_bit_cast(float, (int)b[0]) + __builtin_bit_cast(float, (int)b[1]);
 }
 
+// Max and sum of a float over the whole wave, every lane receiving the same
+// bits: the DPP steps within each 16-lane row, then the row-swap steps.
+__device__ __forceinline__ float wave_max_f(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));
+  x = fmaxf(x, dpp_f<0x4E>(x));
+  x = fmaxf(x, dpp_f<0x141>(x));
+  x = fmaxf(x, dpp_f<0x140>(x));
+  return rows4_max(x);
+}
+__device__ __forceinline__ float wave_sum_f(float x) { return rows4_sum(row16_sum(x)); }
+
 // Min of an int over the whole wave, every lane receiving it: DPP steps
 // within each 16-lane row (as row16_sum), then the row-swap instructions
 // across rows. VALU only. Every lane must be active.
@@ -154,12 +165,6 @@ __device__ __forceinline__ int wave_min_i(int x) {
   x = min((int)a[0], (int)a[1]);
   const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
   return min((int)b[0], (int)b[1]);
-}
-
-// xor shuffle across the whole wave (through ds_bpermute)
-__device__ __forceinline__ float shfl_xor_f(float x, int m) {
-  int lane = __lane_id();
-  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ m) << 2, __builtin_bit_cast(int, x)));
 }
 
 }  // namespace pa
