@@ -28,6 +28,10 @@ Other workloads (``--workload``), same machinery:
 One step = the workload's whole path, all inputs resident in HBM:
 reshape_and_cache of the step's new tokens, [prefill,] then split-K decode
 (partition kernel + reduction kernel) with an output in the input dtype.
+The pure decode steps (llama7b, mixed256: one new token per sequence) write
+their new tokens from inside the partition kernel
+(paged_attention_decode_with_cache_write, bit-identical to the separate
+write); --separate-cache-write launches reshape_and_cache first instead.
 The timed steps replay the step captured as a HIP graph (checked
 bit-identical to the eager step); --eager times plain launches instead. The
 mixed step is timed as one pa_attention_step call with the prefill on a
@@ -67,9 +71,9 @@ WARM_LEAD_CYCLES_PER_STEP = 1_000_000  # spin before the back-to-back eager pass
 CPU_SECONDS = 10.0  # the oracle repeats its pass until about this much CPU time has elapsed
 
 WORKLOADS = {
-    "llama7b": "llama7b_decode_step: reshape_and_cache of 64 new tokens + split-K paged decode, 64 seqs x 32 heads "
+    "llama7b": "llama7b_decode_step: cache write of 64 new tokens + split-K paged decode, 64 seqs x 32 heads "
                "x 128, f16, block_size 16, ctx U[128,2048], seed 393",
-    "mixed256": "mixed256_decode_step: reshape_and_cache of 256 new tokens + split-K paged decode, 256 seqs x 32 "
+    "mixed256": "mixed256_decode_step: cache write of 256 new tokens + split-K paged decode, 256 seqs x 32 "
                 "heads x 128, bf16, block_size 32, ctx lognormal(mean 600) clipped to [1,4096], 1.25x pool, seed 394",
     "prefix13b": "prefix13b_decode_step: 32 prompts x 8 samples sharing a 1024-token prompt's blocks, tails "
                  "U[0,256], 40 heads x 128, f16, block_size 16, seed 395",
@@ -85,10 +89,11 @@ PREFILL_METRIC = "causal paged prefill achieved TFLOP/s (% of the dense MFMA pea
 PREFILL_F32_METRIC = "causal paged prefill achieved TFLOP/s (% of the dense fp32 MFMA peak)"
 
 
-def traffic_file(workload, shared=False):
+def traffic_file(workload, shared=False, separate_write=False):
     if workload in PREFILL_WORKLOADS:
         return os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
     tag = workload + ("_shared" if shared else "_plain" if workload == "prefix13b" else "")
+    tag += "_separate_write" if separate_write else ""
     return os.path.join(ROOT, "profiles", f"decode_{tag}_traffic.json")
 
 
@@ -142,7 +147,7 @@ def _counter_rows(path):
     return rows
 
 
-def record_traffic(workload, shared, fetch_dir, write_dir, copy_bytes):
+def record_traffic(workload, shared, fetch_dir, write_dir, copy_bytes, separate_write=False):
     """Turn two counter runs of this benchmark (FETCH_SIZE, then WRITE_SIZE;
     both in KiB per dispatch) into HBM bytes per launch of the dominant
     kernel, each scaled by what the same counter reads for the plain device
@@ -160,13 +165,14 @@ def record_traffic(workload, shared, fetch_dir, write_dir, copy_bytes):
                      "dispatches": len(part)}
     fetch = out["fetch"]["partition_kernel_kib_avg"] * 1024 * out["fetch"]["scale"]
     write = out["write"]["partition_kernel_kib_avg"] * 1024 * out["write"]["scale"]
-    flags = f"--workload {workload}" + (" --plain" if workload == "prefix13b" and not shared else "")
+    flags = f"--workload {workload}" + (" --plain" if workload == "prefix13b" and not shared else "") + (
+        " --separate-cache-write" if separate_write else "")
     rec = {"kernel": kname, "workload": f"{workload} (bench.py {flags})",
            "kernel_source_sha256": kernel_source_hash(shared, workload), "hbm_bytes_per_launch": round(fetch + write),
            "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write), "counters": out}
     import paged_kv_cache_391_amd as pa
     rec["partition_tokens"] = pa.decode_partition_tokens()
-    with open(traffic_file(workload, shared), "w") as f:
+    with open(traffic_file(workload, shared, separate_write), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec, indent=1))
 
@@ -517,6 +523,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--plain", action="store_true", help="prefix13b: ordinary decode instead of the shared-prefix call")
+    ap.add_argument("--separate-cache-write", action="store_true",
+                    help="llama7b/mixed256: reshape_and_cache as its own launch before the decode")
     ap.add_argument("--block-size", type=int, default=None,
                     help="llama7b: block size (8/16/32/64) for the block-size trade-off; default 16")
     ap.add_argument("--copy-probe-gib", type=float, default=1.0, help="size of the plain-copy bandwidth probe")
@@ -529,7 +537,7 @@ def main():
     args = ap.parse_args()
     if args.record_traffic:
         record_traffic(args.workload, args.workload == "prefix13b" and not args.plain, args.record_traffic[0],
-                       args.record_traffic[1], int(args.copy_probe_gib * (1 << 30)))
+                       args.record_traffic[1], int(args.copy_probe_gib * (1 << 30)), args.separate_cache_write)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         log("bench.py measures one GPU only: each GPU would run this path on its own share of sequences or "
@@ -557,6 +565,8 @@ def main():
     t = time.time()
     if args.block_size is not None and args.workload != "llama7b":
         raise SystemExit("--block-size applies to the llama7b workload only")
+    if args.separate_cache_write and args.workload not in ("llama7b", "mixed256"):
+        raise SystemExit("--separate-cache-write applies to the pure decode workloads (llama7b, mixed256)")
     if args.block_size is not None:
         wl = config2(block_size=args.block_size)
     else:
@@ -580,11 +590,16 @@ def main():
     out = torch.empty_like(od.q)  # output in the input dtype: the production path
     pf_out = torch.empty_like(od.pf_q) if p is not None else None
     P = pa.decode_partition_tokens()
+    # one new token per sequence, at its last position: the partition kernel writes it
+    fused = args.workload in ("llama7b", "mixed256") and not args.separate_cache_write
+    if fused:
+        assert tuple(od.new_k.shape) == tuple(od.q.shape) and int(od.slot_mapping.shape[0]) == S
 
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        pa.reshape_and_cache(od.new_k, od.new_v, od.k_cache, od.v_cache, od.slot_mapping)
+        if not fused:
+            pa.reshape_and_cache(od.new_k, od.new_v, od.k_cache, od.v_cache, od.slot_mapping)
         if ev is not None:
             ev[1].record()
         if p is not None:
@@ -598,6 +613,17 @@ def main():
                                                     od.context_lens, gs, pl, wl.scale, maxctx, nsamp, max_prefix, ws)
             if ev is not None:
                 ev[3].record()
+                ev[4].record()
+        elif fused:
+            pa.paged_attention_decode_with_cache_write_partitions(out, od.q, od.k_cache, od.v_cache, od.new_k,
+                                                                  od.new_v, od.slot_mapping, od.block_tables,
+                                                                  od.context_lens, wl.scale, maxctx, ws)
+            if ev is not None:
+                ev[3].record()
+            pa.paged_attention_decode_with_cache_write_reduce(out, od.q, od.k_cache, od.v_cache, od.new_k, od.new_v,
+                                                              od.slot_mapping, od.block_tables, od.context_lens,
+                                                              wl.scale, maxctx, ws)
+            if ev is not None:
                 ev[4].record()
         else:
             pa.paged_attention_decode_partitions(out, od.q, od.k_cache, od.v_cache, od.block_tables,
@@ -614,6 +640,8 @@ def main():
     t_valid = int((wl.new.slot_mapping >= 0).sum())
     cache_write_bytes = 4 * t_valid * H * D * elt + 4 * T
     k2_bytes = partition_kernel_bytes(d.context_lens, H, D, elt, bs, P)
+    if fused:
+        k2_bytes += cache_write_bytes  # the new tokens read and written, their slots read
     pf_flops, pf_bytes = prefill_work(p, H, D, elt) if p is not None else (0, 0)
     logical_kv = kv
     if args.workload == "prefix13b":
@@ -730,7 +758,7 @@ def main():
     k2_gbps = k2_bytes / (k2_cold_ms * 1e-3) / 1e9
     k2_warm_gbps = k2_bytes / (k2_ms * 1e-3) / 1e9
     log(f"[bench] {ms_per_step * 1e3:.1f} us/step ({'graph' if not args.eager else 'eager'}; eager "
-        f"{eager_ms * 1e3:.1f} us): cache write {cw_ms * 1e3:.1f} us"
+        f"{eager_ms * 1e3:.1f} us): cache write " + ("in the partition kernel" if fused else f"{cw_ms * 1e3:.1f} us")
         + (f", prefill {pf_ms * 1e3:.1f} us ({pf_flops / (pf_ms * 1e-3) / 1e12:.0f} TFLOP/s)" if p else "")
         + f", partition kernel {k2_ms * 1e3:.1f} us warm ({k2_warm_gbps:.0f} GB/s), {k2_cold_ms * 1e3:.1f} us "
           f"cold ({k2_gbps:.0f} GB/s), reduction {k3_ms * 1e3:.1f} us, "
@@ -742,7 +770,7 @@ def main():
     copy_gbps = plain_copy_GBps(args.copy_probe_gib)
 
     traffic = None
-    tf = traffic_file(args.workload, shared)
+    tf = traffic_file(args.workload, shared, args.separate_cache_write)
     if os.path.exists(tf):
         rec = json.load(open(tf))
         if rec.get("kernel_source_sha256") == kernel_source_hash(shared) and rec.get("partition_tokens") == P:
@@ -777,7 +805,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(k2_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(k2_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": ("shared-prefix decode call (shared, tail and reduction kernels)" if shared
-                                else f"decode_partition_kernel<{wl.dtype},{D},{bs}>"),
+                                else f"decode_partition_kernel<{wl.dtype},{D},{bs}>"
+                                + (" with the cache write" if fused else "")),
                      "bytes_per_launch": k2_bytes, "avg_launch_us": round(k2_cold_ms * 1e3, 2),
                      "timing": f"HIP events on the launch stream around each of {args.steps} eager launches, "
                                f"each after a GPU spin (the launches queued ahead) and a {args.evict_mib} MiB "
@@ -790,8 +819,9 @@ def main():
         "cold_step_us": pct(cold_step),
         "hbm_copy_probe_GBps": round(copy_gbps, 1),
         "step_bytes": step_bytes,
-        "phases_us": {"reshape_and_cache": round(cw_ms * 1e3, 2), "decode_partitions": round(k2_ms * 1e3, 2),
-                      "decode_reduce": round(k3_ms * 1e3, 2)},
+        "phases_us": ({"decode_partitions_with_cache_write": round(k2_ms * 1e3, 2)} if fused else
+                      {"reshape_and_cache": round(cw_ms * 1e3, 2), "decode_partitions": round(k2_ms * 1e3, 2)})
+                     | {"decode_reduce": round(k3_ms * 1e3, 2)},
         "cpu_baseline": cpu,
     }
     if args.block_size is not None:

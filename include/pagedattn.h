@@ -237,6 +237,39 @@ pa_status pa_paged_attention_decode(void* out, pa_dtype out_dtype, const void* q
                                     hipStream_t stream);
 
 /*
+ * paged_attention_decode_with_cache_write -- a decode step's cache write and
+ * attention in one launch. A decode step appends each sequence's new token
+ * to its last block and then attends over everything cached (devpress page,
+ * workflow steps "分页加载" and the PagedAttention section; betteryeah page,
+ * section 2.2 for the on-demand blocks, 2.4 for attention across pages).
+ * Here the wave of the partition kernel that holds position
+ * context_lens[s] - 1 takes row s's new token from new_k / new_v instead of
+ * the cache, so no cache-write launch has to finish first, and the call
+ * writes new_k[s] and new_v[s] into slot slot_mapping[s] exactly as
+ * pa_reshape_and_cache puts them (negative slots and slots past the pool
+ * are skipped): the reduction kernel does, when the call is split, else
+ * the partition kernel.
+ *   new_k, new_v   [num_seqs][num_heads][head_dim], dtype
+ *   slot_mapping   int32 [num_seqs]
+ *   k_cache, v_cache are written (the new tokens' slots only).
+ * Other arguments, layouts and errors as for pa_paged_attention_decode; also
+ * INVALID_ARG for a null new_k, new_v or slot_mapping.
+ * Precondition beyond those of pa_paged_attention_decode: a non-negative
+ * slot_mapping[s] is the slot of position context_lens[s] - 1 in row s's
+ * table, read by no other row, and no two rows share a slot (as in a decode
+ * step; a negative one means the row has no new token and reads the cache
+ * as it is). Then out and the caches equal, bit for bit, those of
+ * pa_reshape_and_cache(new_k, new_v, ..., slot_mapping, num_seqs) followed
+ * by pa_paged_attention_decode.
+ */
+pa_status pa_paged_attention_decode_with_cache_write(
+    void* out, pa_dtype out_dtype, const void* q, void* k_cache, void* v_cache, const void* new_k, const void* new_v,
+    const int32_t* slot_mapping, const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+    int32_t max_blocks_per_seq, int32_t max_context_len, float scale, pa_dtype dtype, void* workspace,
+    size_t workspace_bytes, hipStream_t stream);
+
+/*
  * paged_attention_decode_noalloc -- pa_paged_attention_decode with split-K
  * always on and no workspace argument, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops,
@@ -285,6 +318,28 @@ pa_status pa_paged_attention_decode_reduce(void* out, pa_dtype out_dtype, const 
                                            int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                            int32_t max_context_len, pa_dtype dtype, const void* workspace,
                                            size_t workspace_bytes, hipStream_t stream);
+/*
+ * The two stages of pa_paged_attention_decode_with_cache_write, both with
+ * its arguments: _partitions launches K2 (which uses the new tokens, and
+ * writes them into their slots itself when no reduction follows), _reduce
+ * launches K3 (which merges the partials and writes the new tokens) when the
+ * call is split, and returns PA_OK without launching otherwise. Together they
+ * equal pa_paged_attention_decode_with_cache_write bit for bit, outputs and
+ * caches; pa_paged_attention_decode_reduce does not write the tokens and is
+ * no substitute for _reduce here.
+ */
+pa_status pa_paged_attention_decode_with_cache_write_partitions(
+    void* out, pa_dtype out_dtype, const void* q, void* k_cache, void* v_cache, const void* new_k, const void* new_v,
+    const int32_t* slot_mapping, const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+    int32_t max_blocks_per_seq, int32_t max_context_len, float scale, pa_dtype dtype, void* workspace,
+    size_t workspace_bytes, hipStream_t stream);
+pa_status pa_paged_attention_decode_with_cache_write_reduce(
+    void* out, pa_dtype out_dtype, const void* q, void* k_cache, void* v_cache, const void* new_k, const void* new_v,
+    const int32_t* slot_mapping, const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+    int32_t max_blocks_per_seq, int32_t max_context_len, float scale, pa_dtype dtype, void* workspace,
+    size_t workspace_bytes, hipStream_t stream);
 
 /*
  * paged_attention_decode_shared_prefix -- decode for batches in which groups

@@ -78,6 +78,9 @@ def lib():
         dec = [P, ctypes.c_int, P, P, P, P, P, I, I, I, I, I, I, I, I, F, ctypes.c_int, P, Z, P]
         L.pa_paged_attention_decode.argtypes = dec
         L.pa_paged_attention_decode_partitions.argtypes = dec
+        L.pa_paged_attention_decode_with_cache_write.argtypes = dec[:5] + [P, P, P] + dec[5:]
+        L.pa_paged_attention_decode_with_cache_write_partitions.argtypes = dec[:5] + [P, P, P] + dec[5:]
+        L.pa_paged_attention_decode_with_cache_write_reduce.argtypes = dec[:5] + [P, P, P] + dec[5:]
         L.pa_paged_attention_decode_noalloc.argtypes = dec[:17] + [P]
         L.pa_paged_attention_decode_noalloc.restype = ctypes.c_int
         L.pa_decode_noalloc_scratch_bytes.argtypes = []
@@ -113,6 +116,9 @@ def lib():
                      "pa_allocator_take_copies"):
             getattr(L, name).restype = ctypes.c_int
         for name in ("pa_reshape_and_cache", "pa_gather_kv", "pa_paged_attention_decode",
+                     "pa_paged_attention_decode_with_cache_write",
+                     "pa_paged_attention_decode_with_cache_write_partitions",
+                     "pa_paged_attention_decode_with_cache_write_reduce",
                      "pa_paged_attention_decode_partitions", "pa_paged_attention_decode_reduce",
                      "pa_paged_attention_prefill"):
             getattr(L, name).restype = ctypes.c_int
@@ -309,6 +315,55 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     split-K over long contexts. Pass ``max_context_len`` to avoid a sync."""
     _check("paged_attention_decode", lib().pa_paged_attention_decode(
         *_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, workspace)))
+
+
+def paged_attention_decode_with_cache_write(out, q, k_cache, v_cache, new_k, new_v, slot_mapping, block_tables,
+                                            context_lens, scale: float, max_context_len: int | None = None,
+                                            workspace=None):
+    """One decode step in one launch: ``reshape_and_cache(new_k, new_v,
+    k_cache, v_cache, slot_mapping)`` (one new token per sequence, at
+    position ``context_lens[s] - 1``) followed by ``paged_attention_decode``,
+    with the same outputs and caches bit for bit."""
+    args = _decode_with_cache_write_args(out, q, k_cache, v_cache, new_k, new_v, slot_mapping, block_tables,
+                                         context_lens, scale, max_context_len, workspace)
+    _check("paged_attention_decode_with_cache_write", lib().pa_paged_attention_decode_with_cache_write(*args))
+
+
+def paged_attention_decode_with_cache_write_partitions(out, q, k_cache, v_cache, new_k, new_v, slot_mapping,
+                                                       block_tables, context_lens, scale: float,
+                                                       max_context_len: int, workspace=None):
+    """First stage of ``paged_attention_decode_with_cache_write`` (the
+    partition kernel, which uses the new tokens);
+    ``paged_attention_decode_with_cache_write_reduce`` is the second."""
+    args = _decode_with_cache_write_args(out, q, k_cache, v_cache, new_k, new_v, slot_mapping, block_tables,
+                                         context_lens, scale, max_context_len, workspace)
+    _check("paged_attention_decode_with_cache_write_partitions",
+           lib().pa_paged_attention_decode_with_cache_write_partitions(*args))
+
+
+def paged_attention_decode_with_cache_write_reduce(out, q, k_cache, v_cache, new_k, new_v, slot_mapping,
+                                                   block_tables, context_lens, scale: float, max_context_len: int,
+                                                   workspace=None):
+    """Second stage of ``paged_attention_decode_with_cache_write`` (the
+    reduction, which also writes the new tokens into their slots; nothing
+    when the call is not split). Same arguments as the first stage."""
+    args = _decode_with_cache_write_args(out, q, k_cache, v_cache, new_k, new_v, slot_mapping, block_tables,
+                                         context_lens, scale, max_context_len, workspace)
+    _check("paged_attention_decode_with_cache_write_reduce",
+           lib().pa_paged_attention_decode_with_cache_write_reduce(*args))
+
+
+def _decode_with_cache_write_args(out, q, k_cache, v_cache, new_k, new_v, slot_mapping, block_tables, context_lens,
+                                  scale, max_context_len, workspace):
+    _dev(new_k, new_v, slot_mapping)
+    _i32(slot_mapping)
+    S = int(context_lens.shape[0])
+    if (new_k.shape != q.shape or new_v.shape != q.shape or new_k.dtype != k_cache.dtype
+            or new_v.dtype != k_cache.dtype or tuple(slot_mapping.shape) != (S,)):
+        raise ValueError("new_k and new_v must be [num_seqs, num_heads, head_dim] in the cache dtype, "
+                         "slot_mapping [num_seqs]")
+    args = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, workspace)
+    return (*args[:5], _ptr(new_k), _ptr(new_v), _ptr(slot_mapping), *args[5:])
 
 
 def decode_noalloc_scratch_bytes() -> int:

@@ -102,7 +102,7 @@ float* scratch_on_device() {
 }
 
 struct DecodeCall {
-  pa::DecodeArgs args;
+  pa::DecodeArgs args{};
   Dt dt;
   int D, BS;
   bool split;
@@ -144,6 +144,7 @@ pa_status prepare_decode(DecodeCall& call, void* out, pa_dtype out_dtype, const 
   a.max_blocks = max_blocks_per_seq;
   a.max_ctx = max_context_len;
   a.num_blocks = num_blocks;
+  a.block_size = block_size;
   a.max_parts = (int)grid_parts;
   a.ws_parts = (int)grid_parts;
   // without split-K one partition spans the longest context
@@ -290,6 +291,76 @@ pa_status pa_paged_attention_decode(void* out, pa_dtype out_dtype, const void* q
   hipError_t e = pa::launch_decode_partitions(call.args, call.dt, call.D, call.BS, pa::RowMode::Decode, stream);
   if (e == hipSuccess && call.split) e = pa::launch_decode_reduce(call.args, call.dt, call.D, false, stream);
   return hip_status(e);
+}
+
+namespace {
+// The decode call of pa_paged_attention_decode_with_cache_write: a plain
+// decode call that also carries the new tokens.
+pa_status prepare_decode_with_cache_write(DecodeCall& call, void* out, pa_dtype out_dtype, const void* q,
+                                          void* k_cache, void* v_cache, const void* new_k, const void* new_v,
+                                          const int32_t* slot_mapping, const int32_t* block_tables,
+                                          const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                          int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                                          float scale, pa_dtype dtype, void* workspace, size_t workspace_bytes) {
+  pa_status st = prepare_decode(call, out, out_dtype, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                                num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                max_context_len, scale, dtype, workspace, workspace_bytes);
+  if (st != PA_OK || num_seqs == 0) return st;
+  if (!new_k || !new_v || !slot_mapping) return PA_ERR_INVALID_ARG;
+  call.args.new_k = new_k;
+  call.args.new_v = new_v;
+  call.args.slot_mapping = slot_mapping;
+  call.args.write_in_reduce = call.split ? 1 : 0;  // K3 stores the tokens when it runs; K2 otherwise
+  return PA_OK;
+}
+}  // namespace
+
+pa_status pa_paged_attention_decode_with_cache_write(
+    void* out, pa_dtype out_dtype, const void* q, void* k_cache, void* v_cache, const void* new_k, const void* new_v,
+    const int32_t* slot_mapping, const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+    int32_t max_blocks_per_seq, int32_t max_context_len, float scale, pa_dtype dtype, void* workspace,
+    size_t workspace_bytes, hipStream_t stream) {
+  DecodeCall call;
+  pa_status st = prepare_decode_with_cache_write(call, out, out_dtype, q, k_cache, v_cache, new_k, new_v,
+                                                 slot_mapping, block_tables, context_lens, num_seqs, num_heads,
+                                                 num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                                 max_context_len, scale, dtype, workspace, workspace_bytes);
+  if (st != PA_OK || num_seqs == 0) return st;
+  hipError_t e = pa::launch_decode_partitions(call.args, call.dt, call.D, call.BS, pa::RowMode::Decode, stream);
+  if (e == hipSuccess && call.split) e = pa::launch_decode_reduce(call.args, call.dt, call.D, false, stream);
+  return hip_status(e);
+}
+
+pa_status pa_paged_attention_decode_with_cache_write_partitions(
+    void* out, pa_dtype out_dtype, const void* q, void* k_cache, void* v_cache, const void* new_k, const void* new_v,
+    const int32_t* slot_mapping, const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+    int32_t max_blocks_per_seq, int32_t max_context_len, float scale, pa_dtype dtype, void* workspace,
+    size_t workspace_bytes, hipStream_t stream) {
+  DecodeCall call;
+  pa_status st = prepare_decode_with_cache_write(call, out, out_dtype, q, k_cache, v_cache, new_k, new_v,
+                                                 slot_mapping, block_tables, context_lens, num_seqs, num_heads,
+                                                 num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                                 max_context_len, scale, dtype, workspace, workspace_bytes);
+  if (st != PA_OK || num_seqs == 0) return st;
+  return hip_status(pa::launch_decode_partitions(call.args, call.dt, call.D, call.BS, pa::RowMode::Decode, stream));
+}
+
+pa_status pa_paged_attention_decode_with_cache_write_reduce(
+    void* out, pa_dtype out_dtype, const void* q, void* k_cache, void* v_cache, const void* new_k, const void* new_v,
+    const int32_t* slot_mapping, const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+    int32_t max_blocks_per_seq, int32_t max_context_len, float scale, pa_dtype dtype, void* workspace,
+    size_t workspace_bytes, hipStream_t stream) {
+  DecodeCall call;
+  pa_status st = prepare_decode_with_cache_write(call, out, out_dtype, q, k_cache, v_cache, new_k, new_v,
+                                                 slot_mapping, block_tables, context_lens, num_seqs, num_heads,
+                                                 num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                                 max_context_len, scale, dtype, workspace, workspace_bytes);
+  if (st != PA_OK || num_seqs == 0 || !call.split) return st;
+  return hip_status(pa::launch_decode_reduce(call.args, call.dt, call.D, false, stream));
 }
 
 size_t pa_decode_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }

@@ -63,10 +63,41 @@ __global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_kernel(const 
   const int row = blockIdx.x / hg;
   const int h = (blockIdx.x % hg) * NW + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (h >= a.H) return;
+  const int lane = threadIdx.x & 63;
+  // The fused cache write of a decode step, when a reduction follows the
+  // partition kernel: this (row, head)'s new token, which the partition
+  // kernel read from new_k/new_v, goes into its slot here. 16 bytes per lane
+  // for K and for V, read first and stored last (padding slots and slots
+  // past the pool are skipped).
+  constexpr int TOKEN_LANES = D * ElemT<DT>::bytes / 16;
+  bool write_token = false;
+  int64_t token_dst = 0;
+  u32x4 tk{}, tv{};
+  if constexpr (MODE == RowMode::Decode) {
+    if (a.write_in_reduce) {
+      const int32_t slot = a.slot_mapping[row];
+      write_token = slot >= 0 && slot < a.num_blocks * a.block_size && lane < TOKEN_LANES;
+      if (write_token) {
+        const int64_t src = ((int64_t)row * a.H + h) * D * ElemT<DT>::bytes + lane * 16;
+        tk = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a.new_k) + src);
+        tv = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a.new_v) + src);
+        token_dst = kv_row_offset(slot / a.block_size, h, slot % a.block_size, a.H, a.block_size, D) *
+                        ElemT<DT>::bytes + lane * 16;
+      }
+    }
+  }
+  auto store_token = [&]() {
+    if (write_token) {
+      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(const_cast<void*>(a.k_cache)) + token_dst) = tk;
+      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(const_cast<void*>(a.v_cache)) + token_dst) = tv;
+    }
+  };
   const int ctx = row_ctx(a, row);
   const int nparts = row_parts<MODE>(a, row, ctx).total();
-  if (nparts <= 1) return;
-  const int lane = threadIdx.x & 63;
+  if (nparts <= 1) {
+    store_token();
+    return;
+  }
   const int64_t prow = ((int64_t)row * a.H + h) * a.ws_parts;
   const float* ml = a.ws + (int64_t)a.num_rows * a.H * a.ws_parts * D + prow * 2;
   const float* acc = a.ws + prow * D;
@@ -113,6 +144,7 @@ __global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_kernel(const 
   const int64_t orow = ((int64_t)row * a.H + h) * D;
 #pragma unroll
   for (int i = 0; i < PER; ++i) store_out<DT>(a.out, orow + lane + 64 * i, x[i] / Lsum, a.out_f32);
+  store_token();
 }
 
 template <Dt DT, int D, int BS, RowMode MODE>

@@ -49,6 +49,17 @@ template <Dt DT, int D> struct Lane {
     }
   }
 
+  // the lane's words of one row written back in the layout load() reads
+  __device__ static __forceinline__ void store(const uint32_t (&w)[WPL], char* base, uint32_t lane_off) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      if constexpr (VB == 16)
+        *reinterpret_cast<u32x4*>(base + lane_off + j * 16 * VB) = u32x4{w[j * 4], w[j * 4 + 1], w[j * 4 + 2], w[j * 4 + 3]};
+      else
+        *reinterpret_cast<u32x2*>(base + lane_off + j * 16 * VB) = u32x2{w[j * 2], w[j * 2 + 1]};
+    }
+  }
+
   __device__ static __forceinline__ float dot(const uint32_t (&q)[WPL], const uint32_t (&k)[WPL]) {
     float acc = 0.f;
 #pragma unroll
@@ -258,6 +269,99 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int b
   const int u0 = (rp.tok0 >> 4) + part * a.part_tiles;
   const int my_tiles = max(0, min(n_tiles, u0 + a.part_tiles) - u0);
 
+  // Fused cache write (decode rows, new_k set): row `row`'s new token sits at
+  // position ctx - 1, in the final tile of the row's last partition. That
+  // partition's wave fetches the token's K and V rows from new_k/new_v into
+  // LDS right behind its first tile (DMA: no registers held across the tile
+  // loop, the fetch is long done when the final tile comes, and the slot
+  // read that decides it waits behind the table and tile loads, not in front
+  // of them) and uses them in place of the final tile's cache row, so no
+  // other kernel has to run first. The slot itself (padding slots and slots
+  // past the pool are skipped, and the row then reads the cache as it is) is
+  // written by the reduction kernel when one follows: a store in this
+  // read-bound kernel costs far more than its bytes (an extra 512 B per wave
+  // measured ~10 us over 8k waves). Without a reduction the wave stores
+  // them itself, after its output.
+  // K row at [0, ROW_BYTES), V row at [1024, 1024 + ROW_BYTES) of the wave's
+  // 2 KiB; the rest of each KiB takes the DMA's unused lanes
+  __shared__ __align__(16) uint8_t ntok[MODE == RowMode::Decode ? HG : 1][2048];
+  static_assert(L::ROW_BYTES <= 1024, "a row fits one DMA");
+  bool last_part = false;
+  if constexpr (MODE == RowMode::Decode) last_part = a.new_k != nullptr && part == max(rp.own, 1) - 1;
+  // The slot, read unconditionally (another row-indexed array stands in when
+  // there is no slot to read) with a vector load: a scalar load would be
+  // waited for together with the kernel arguments, ahead of the table and
+  // tile loads; a vector load is done by the time the table entries are.
+  int32_t slot_v;
+  {
+    int32_t zero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+    slot_v = (last_part ? a.slot_mapping + row : a.context_lens + row)[zero];
+  }
+  // the slot at the point of use (what is computed from it is not hoisted
+  // ahead of the loads issued before that point)
+  auto slot_here = [&]() {
+    int32_t v = slot_v;
+    asm volatile("" : "+v"(v));
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  auto fused = [&]() {
+    const int32_t sl = slot_here();
+    return last_part && sl >= 0 && sl < a.num_blocks * BS;
+  };
+  auto fetch_new_token = [&]() {
+    const int64_t new_src = ((int64_t)row * a.H + h) * L::ROW_BYTES;
+    const uint32_t voff = (uint32_t)((lane * 16) % L::ROW_BYTES);
+    const uint32_t lds = lds_offset(&ntok[wave][0]);
+    lds_dma16s(reinterpret_cast<const char*>(a.new_k) + new_src, voff, lds);
+    lds_dma16s(reinterpret_cast<const char*>(a.new_v) + new_src, voff, lds + 1024);
+  };
+  // the lane's words of the new token's K or V row (in the lane layout of a
+  // tile row), out of LDS
+  auto token_words = [&](uint32_t (&w)[WPL], int kv) {
+    const uint8_t* const src = &ntok[wave][kv * 1024];
+#pragma unroll
+    for (int j = 0; j < L::NV; ++j)
+#pragma unroll
+      for (int x = 0; x < L::VW; ++x)
+        w[j * L::VW + x] = *reinterpret_cast<const uint32_t*>(src + c * L::VB + j * 16 * L::VB + 4 * x);
+  };
+  // The token's rows, once every earlier load (the DMA among them) is done;
+  // the caller needs the last tile's loads next anyway.
+  auto new_token = [&](uint32_t (&nk)[WPL], uint32_t (&nv)[WPL]) {
+    wait_vmcnt0();
+    token_words(nk, 0);
+    token_words(nv, 1);
+  };
+  // Row group 0 stores the token into its slot as the wave's last act: the
+  // compiler counts stores with the loads, so a store ahead of the tile
+  // math would make the wave wait for its write to complete.
+  auto store_new_token = [&]() {
+    uint32_t w[WPL];
+    const int32_t sl = slot_here();
+    const int64_t dst = kv_row_offset(sl / BS, h, sl % BS, a.H, BS, D) * L::EB;
+    const uint32_t lo = (uint32_t)(c * L::VB);
+    token_words(w, 0);
+    L::store(w, const_cast<char*>(reinterpret_cast<const char*>(a.k_cache)) + dst, lo);
+    token_words(w, 1);
+    L::store(w, const_cast<char*>(reinterpret_cast<const char*>(a.v_cache)) + dst, lo);
+  };
+  // the final tile's row (ctx - 1) % 16 is held by load j = r / 4 of the
+  // lanes of row group r % 4: they take the new token's words instead. The
+  // token is read into the first row of the other, already consumed buffer
+  // (no registers beyond the two tile buffers).
+  auto fuse_tile = [&](uint32_t (&kw)[4][WPL], uint32_t (&vw)[4][WPL], uint32_t (&nk)[WPL], uint32_t (&nv)[WPL]) {
+    new_token(nk, nv);
+    const int r = (ctx - 1) & 15;
+    const bool mine = g == (r & 3);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int w = 0; w < WPL; ++w) {
+        kw[j][w] = (mine && j == (r >> 2)) ? nk[w] : kw[j][w];
+        vw[j][w] = (mine && j == (r >> 2)) ? nv[w] : vw[j][w];
+      }
+  };
   uint32_t qw[WPL];
   L::load(qw, reinterpret_cast<const char*>(a.q) + ((int64_t)row * a.H + h) * L::ROW_BYTES, (uint32_t)(c * L::VB));
 
@@ -316,6 +420,7 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int b
     uint32_t ka[4][WPL], va[4][WPL], kb[4][WPL], vb[4][WPL];
     int ta, tb0;
     load_tile(ka, va, tile_off(0, ta));
+    if (fused() && base == 0) fetch_new_token();
     int i = 0;
     for (; i + 2 < cnt; i += 2) {
       load_tile(kb, vb, tile_off(i + 1, tb0));
@@ -323,13 +428,20 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int b
       load_tile(ka, va, tile_off(i + 2, ta));
       consume_tile<DT, D>(st, qw, kb, vb, tb0, ctx, g, a.scale_log2);
     }
+    const bool fuse_here = fused() && base + 64 >= my_tiles;  // this chunk ends with the row's final tile
     if (i + 1 < cnt) {
       load_tile(kb, vb, tile_off(i + 1, tb0));
       consume_tile<DT, D>(st, qw, ka, va, ta, ctx, g, a.scale_log2);
+      if (fuse_here) fuse_tile(kb, vb, ka[0], va[0]);
       consume_tile<DT, D>(st, qw, kb, vb, tb0, ctx, g, a.scale_log2);
     } else {
+      if (fuse_here) fuse_tile(ka, va, kb[0], vb[0]);
       consume_tile<DT, D>(st, qw, ka, va, ta, ctx, g, a.scale_log2);
     }
+  }
+  if (fused() && my_tiles == 0 && !a.write_in_reduce) {  // an empty context still has its token written
+    fetch_new_token();
+    wait_vmcnt0();
   }
 
   // merge the four 16-lane rows of the wave (same lane column c) with the
@@ -362,6 +474,7 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int b
       ml[1] = st.l;
     }
   }
+  if (fused() && !a.write_in_reduce) store_new_token();
 }
 
 }  // namespace pa

@@ -167,4 +167,26 @@ __device__ __forceinline__ int wave_min_i(int x) {
   return min((int)b[0], (int)b[1]);
 }
 
+// LDS byte offset of a __shared__ object
+template <typename T> __device__ __forceinline__ uint32_t lds_offset(T* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)p;
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane L's bytes
+// land at LDS byte offset lds_off + 16 L (lds_off wave-uniform, via M0);
+// the source is a wave-uniform 64-bit base in SGPRs plus a 32-bit per-lane
+// byte offset, so the address adds happen in the load, not in VALU.
+// Written as inline assembly so that the compiler, which waits for every
+// such load before any later LDS read, leaves the waits to the kernel; the
+// loads count in vmcnt like any vector load. M0 is written in the same
+// assembly block as the load that reads it (one wait state between them),
+// and the kernels that use it use M0 nowhere else, so clobbering a register
+// the compiler does not preserve around inline assembly loses nothing.
+__device__ __forceinline__ void lds_dma16s(const char* sbase, uint32_t voff, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_off)
+               : "memory", "m0");
+}
+// wait until none of this wave's vector loads is outstanding
+__device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 }  // namespace pa

@@ -77,6 +77,15 @@ struct DecodeArgs {
   int member_chunks;                // shared-prefix kernel: waves per (group, head, partition)
   float scale_log2;                 // scale * log2(e)
   int out_f32;
+  // decode with the fused cache write: row r's new token (K and V rows of
+  // [rows][H][D], slot slot_mapping[r]) is used by K2 as position
+  // context_lens[r] - 1 and written into its slot, by K3 when write_in_reduce
+  // is set (a reduction follows) and by K2 otherwise; nullptr: no write
+  const void* new_k;
+  const void* new_v;
+  const int32_t* slot_mapping;
+  int write_in_reduce;
+  int block_size;
 };
 
 hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,

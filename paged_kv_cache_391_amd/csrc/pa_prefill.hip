@@ -84,20 +84,6 @@ static_assert(NBUF >= 2, "at least one tile in flight");
 constexpr float RESCALE_LOG2 = 8.f; // lazy rescale threshold (log2 units): p < 256 between rescales
 static_assert(KT == 32, "key tile of 32");
 
-// 16 bytes per lane from global memory straight into LDS: lane L's bytes
-// land at LDS byte offset lds_off + 16 L (lds_off wave-uniform, via M0);
-// the source is a wave-uniform 64-bit base in SGPRs plus a 32-bit per-lane
-// byte offset, so the address adds happen in the load, not in VALU.
-// Written as inline assembly so that the compiler, which waits for every
-// such load before any later LDS read, leaves the waits to the kernel; the
-// loads count in vmcnt like any vector load. M0 is written in the same
-// assembly block as the load that reads it (one wait state between them),
-// and the compiled kernel uses M0 nowhere else, so clobbering a register
-// the compiler does not preserve around inline assembly loses nothing.
-__device__ __forceinline__ void lds_dma16s(const char* sbase, uint32_t voff, uint32_t lds_off) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_off)
-               : "memory", "m0");
-}
 // max without the NaN-quieting the compiler adds around values of unknown
 // origin (the scores are never signalling NaNs); the wait states let a
 // following v_permlane read the result
@@ -121,8 +107,6 @@ __device__ __forceinline__ void rows4_max2(float& a, float& b) {
   a = __builtin_bit_cast(float, (int)s3[0]);
   b = __builtin_bit_cast(float, (int)s3[1]);
 }
-// wait until none of this wave's vector loads is outstanding
-__device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Block ids through the scalar cache, as inline assembly: once the DMA
 // assembly is in the kernel the compiler can no longer prove the table
 // unchanged and would read it with vector loads, whose waits would drain
@@ -160,9 +144,6 @@ template <Dt DT> __device__ __forceinline__ float dot2one(uint32_t w, uint32_t o
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w), __builtin_bit_cast(half2_t, one2), c, false);
   else
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, w), __builtin_bit_cast(bf162_t, one2), c, false);
-}
-template <typename T> __device__ __forceinline__ uint32_t lds_offset(T* p) {
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)p;
 }
 
 // Work item of this workgroup: sequence s, head h, query tile qt (of QT

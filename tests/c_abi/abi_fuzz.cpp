@@ -67,7 +67,7 @@ int main() {
   CHECK(pa_decode_partition_tokens() > 0 && pa_decode_noalloc_scratch_bytes() > 0);
   for (int it = 0; it < 20000; ++it) {
     pa_status s = PA_OK;
-    switch (rnd(9)) {
+    switch (rnd(12)) {
       case 0:
         s = pa_reshape_and_cache(p(), p(), p(), p(), (const int32_t*)p(), v(), v(), v(), v(), v(), dt(), nullptr);
         break;
@@ -95,6 +95,22 @@ int main() {
                                                     (const int32_t*)p(), (const int32_t*)p(), v(), v(), v(), v(), v(),
                                                     v(), v(), v(), v(), v(), v(), f(), dt(), p(),
                                                     (size_t)(uint32_t)v(), nullptr);
+        break;
+      case 8:
+        s = pa_paged_attention_decode_with_cache_write(p(), dt(), p(), p(), p(), p(), p(), (const int32_t*)p(),
+                                                       (const int32_t*)p(), (const int32_t*)p(), v(), v(), v(), v(),
+                                                       v(), v(), v(), v(), f(), dt(), p(), (size_t)(uint32_t)v(),
+                                                       nullptr);
+        break;
+      case 10:
+        s = pa_paged_attention_decode_with_cache_write_reduce(
+            p(), dt(), p(), p(), p(), p(), p(), (const int32_t*)p(), (const int32_t*)p(), (const int32_t*)p(), v(),
+            v(), v(), v(), v(), v(), v(), v(), f(), dt(), p(), (size_t)(uint32_t)v(), nullptr);
+        break;
+      case 9:
+        s = pa_paged_attention_decode_with_cache_write_partitions(
+            p(), dt(), p(), p(), p(), p(), p(), (const int32_t*)p(), (const int32_t*)p(), (const int32_t*)p(), v(),
+            v(), v(), v(), v(), v(), v(), v(), f(), dt(), p(), (size_t)(uint32_t)v(), nullptr);
         break;
       case 7:
         s = pa_paged_attention_prefill(p(), dt(), p(), p(), p(), (const int32_t*)p(), (const int32_t*)p(),

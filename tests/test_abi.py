@@ -204,3 +204,20 @@ def test_noalloc_decode_refuses_past_its_scratch_before_any_launch():
     rc = L.pa_paged_attention_decode_noalloc(FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE, S, H, H, D, 16, 1 << 16,
                                              ctx // 16, ctx, 0.1, 1, NULL)
     assert rc == pa.PA_ERR_SCRATCH_LIMIT
+
+
+def test_fused_decode_requires_its_new_tokens():
+    """The decode with the fused cache write refuses a null new_k, new_v or
+    slot_mapping before any launch, and otherwise validates like the decode
+    (fake pointers: nothing is launched)."""
+    L = pa.lib()
+    S, H, D = 4, 2, 128
+    common = (S, H, H, D, 16, 64, 8, 100, 0.1, 1, NULL, 0, NULL)
+    for fn in (L.pa_paged_attention_decode_with_cache_write, L.pa_paged_attention_decode_with_cache_write_partitions,
+               L.pa_paged_attention_decode_with_cache_write_reduce):
+        for nk, nv, sl in ((NULL, FAKE, FAKE), (FAKE, NULL, FAKE), (FAKE, FAKE, NULL)):
+            assert fn(FAKE, 0, FAKE, FAKE, FAKE, nk, nv, sl, FAKE, FAKE, *common) == pa.PA_ERR_INVALID_ARG
+        # max_context_len past the table: refused like the decode
+        rc = fn(FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, S, H, H, D, 16, 64, 8, 8 * 16 + 1, 0.1, 1,
+                NULL, 0, NULL)
+        assert rc == pa.PA_ERR_INVALID_ARG

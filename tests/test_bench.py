@@ -82,7 +82,7 @@ def test_traffic_record_scales_counters_by_the_plain_copy(tmp_path, monkeypatch,
     write = _counter_csv(str(tmp_path / "w"), [(kernel, 40.0), (kernel, 60.0), (other, 9e9),
                                                ("__amd_rocclr_copyBuffer", 1048576.0)])
     out = tmp_path / "rec.json"
-    monkeypatch.setattr(bench, "traffic_file", lambda w, s=False: str(out))
+    monkeypatch.setattr(bench, "traffic_file", lambda w, s=False, sep=False: str(out))
     bench.record_traffic(workload, shared, fetch, write, copy_bytes)
     rec = json.load(open(out))
     assert rec["fetch_bytes_per_launch"] == round(2000.0 * 1024 * 2.0)  # the copy's FETCH reads half its bytes
@@ -100,6 +100,7 @@ def test_traffic_records_name_the_roofline_kernels():
     assert bench.traffic_file("prefill_long").endswith("prefill_long_traffic.json")
     assert bench.traffic_file("prefix13b", True).endswith("decode_prefix13b_shared_traffic.json")
     assert bench.traffic_file("prefix13b", False).endswith("decode_prefix13b_plain_traffic.json")
+    assert bench.traffic_file("llama7b", False, True).endswith("decode_llama7b_separate_write_traffic.json")
 
 
 @pytest.mark.gpu

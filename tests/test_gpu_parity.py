@@ -232,6 +232,88 @@ def test_decode_rows_of_many_partitions():
     _check_attention(od.decode(torch.float32, split=False), ref, "f16")
 
 
+def _fused_rows(wl, pad_rows=()):
+    """Per-row new tokens (fresh values) and slots for the fused decode: a
+    row with a context gets its last position's slot, a row in pad_rows and
+    an empty row get slot -1 (nothing written; the row reads the cache as
+    it is)."""
+    from workloads import normal
+    d = wl.decode
+    S, H, D = d.q.shape
+    rng = np.random.default_rng(5)
+    nk = normal(rng, (S, H, D), wl.dtype)
+    nv = normal(rng, (S, H, D), wl.dtype)
+    slots = np.full(S, -1, dtype=np.int32)
+    t = 0
+    for r in range(S):
+        if d.context_lens[r] > 0:
+            if r not in pad_rows:
+                slots[r] = wl.new.slot_mapping[t]
+            t += 1
+    return nk, nv, slots
+
+
+def _check_fused(wl, split, pad_rows=()):
+    """pa_paged_attention_decode_with_cache_write against reshape_and_cache
+    followed by paged_attention_decode (outputs and caches bit for bit) and
+    against the oracle. Both caches first hold the workload's own new tokens
+    (so padding rows read finite values); the fresh tokens then replace them."""
+    d = wl.decode
+    nk, nv, slots = _fused_rows(wl, pad_rows)
+    dt = wl.dtype
+    ref = _on_device_written(wl)
+    nk_d, nv_d, sl_d = dev(nk, dt), dev(nv, dt), dev(slots)
+    pa.reshape_and_cache(nk_d, nv_d, ref.k_cache, ref.v_cache, sl_d)
+    out_ref = ref.decode(torch.float32, split=split)
+    od = _on_device_written(wl)
+    out = torch.empty_like(out_ref)
+    ws = pa.make_decode_workspace(d.num_seqs, wl.num_heads, wl.head_dim, d.max_context_len) if split else None
+    pa.paged_attention_decode_with_cache_write(out, od.q, od.k_cache, od.v_cache, nk_d, nv_d, sl_d, od.block_tables,
+                                               od.context_lens, wl.scale, d.max_context_len, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_ref)
+    assert np.array_equal(bits(host(od.k_cache)), bits(host(ref.k_cache)))
+    assert np.array_equal(bits(host(od.v_cache)), bits(host(ref.v_cache)))
+    if ws is not None:  # the two stages, as a caller that times them runs them
+        st = _on_device_written(wl)
+        out_st = torch.empty_like(out_ref)
+        pa.paged_attention_decode_with_cache_write_partitions(out_st, st.q, st.k_cache, st.v_cache, nk_d, nv_d, sl_d,
+                                                              st.block_tables, st.context_lens, wl.scale,
+                                                              d.max_context_len, ws)
+        pa.paged_attention_decode_with_cache_write_reduce(out_st, st.q, st.k_cache, st.v_cache, nk_d, nv_d, sl_d,
+                                                          st.block_tables, st.context_lens, wl.scale,
+                                                          d.max_context_len, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out_st, out)
+        assert np.array_equal(bits(host(st.k_cache)), bits(host(ref.k_cache)))
+        assert np.array_equal(bits(host(st.v_cache)), bits(host(ref.v_cache)))
+    kc, vc = oracle.reshape_and_cache(wl.new.k, wl.new.v, wl.k_cache, wl.v_cache, wl.new.slot_mapping,
+                                      wl.block_size, dt)
+    kc, vc = oracle.reshape_and_cache(nk, nv, kc, vc, slots, wl.block_size, dt)
+    _check_attention(out, oracle.decode(d.q, kc, vc, d.block_tables, d.context_lens, wl.scale, dt), dt)
+
+
+@pytest.mark.parametrize("cid", [2, 3])
+def test_decode_with_cache_write_full_config(cid):
+    """The fused cache write on the LLaMA-7B and 256-sequence workloads (every
+    row's last position is its new token)."""
+    wl, _, _ = _config(cid)
+    _check_fused(wl, split=True)
+
+
+@pytest.mark.parametrize("dtype,D,bs,split", [("f16", 128, 16, True), ("bf16", 128, 8, True), ("f32", 128, 32, True),
+                                              ("f16", 64, 64, False), ("f32", 64, 8, False), ("bf16", 64, 16, True)])
+def test_decode_with_cache_write_ragged(dtype, D, bs, split):
+    """Contexts around tile, block and partition edges (the new token in every
+    row of its tile), empty rows and padding rows (slot -1: nothing written,
+    the row reads the cache as it is)."""
+    P = pa.decode_partition_tokens()
+    ctx = [0, 1, 2, 15, 16, 17, 31, 33, 100, P - 1, P, P + 1, 2 * P + 9, 3 * P, 0, 47]
+    wl = decode_workload(f"fused_{dtype}_{D}_{bs}", 640 + bs, dtype, 3, D, bs, ctx,
+                         maxb=math.ceil(max(ctx) / bs), pool_factor=1.3)
+    _check_fused(wl, split, pad_rows=(7, 12))
+
+
 def test_decode_empty_context_gives_zeros():
     wl = decode_workload("empty", 601, "f16", 2, 128, 16, [0, 5, 0, 40], maxb=4, pool_blocks=8)
     od = _on_device_written(wl)
