@@ -641,7 +641,9 @@ def main():
     cache_write_bytes = 4 * t_valid * H * D * elt + 4 * T
     k2_bytes = partition_kernel_bytes(d.context_lens, H, D, elt, bs, P)
     if fused:
-        k2_bytes += cache_write_bytes  # the new tokens read and written, their slots read
+        # the partition kernel reads the new tokens and their slots; it writes them too only when no
+        # reduction follows (a split call leaves the writes to the reduction kernel)
+        k2_bytes += cache_write_bytes if ws is None else 2 * t_valid * H * D * elt + 4 * T
     pf_flops, pf_bytes = prefill_work(p, H, D, elt) if p is not None else (0, 0)
     logical_kv = kv
     if args.workload == "prefix13b":
