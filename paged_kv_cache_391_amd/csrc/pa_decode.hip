@@ -67,29 +67,29 @@ __global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_kernel(const 
   // The fused cache write of a decode step, when a reduction follows the
   // partition kernel: this (row, head)'s new token, which the partition
   // kernel read from new_k/new_v, goes into its slot here. 16 bytes per lane
-  // for K and for V, read first and stored last (padding slots and slots
-  // past the pool are skipped).
+  // for K and for V, read first (whatever the slot: the rows are always
+  // there, and the loads need not wait for the slot) and stored last, unless
+  // the slot is padding or past the pool.
+  // (The slot is read unconditionally, another row-indexed array standing
+  // in when there is none, so it arrives with the row's length in one round
+  // trip.)
   constexpr int TOKEN_LANES = D * ElemT<DT>::bytes / 16;
-  bool write_token = false;
-  int64_t token_dst = 0;
+  const bool writes = MODE == RowMode::Decode && a.write_in_reduce;
+  const bool token_lane = writes && lane < TOKEN_LANES;
+  const int32_t slot = (writes ? a.slot_mapping : a.context_lens)[row];
   u32x4 tk{}, tv{};
-  if constexpr (MODE == RowMode::Decode) {
-    if (a.write_in_reduce) {
-      const int32_t slot = a.slot_mapping[row];
-      write_token = slot >= 0 && slot < a.num_blocks * a.block_size && lane < TOKEN_LANES;
-      if (write_token) {
-        const int64_t src = ((int64_t)row * a.H + h) * D * ElemT<DT>::bytes + lane * 16;
-        tk = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a.new_k) + src);
-        tv = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a.new_v) + src);
-        token_dst = kv_row_offset(slot / a.block_size, h, slot % a.block_size, a.H, a.block_size, D) *
-                        ElemT<DT>::bytes + lane * 16;
-      }
-    }
+  if (token_lane) {
+    const int64_t src = ((int64_t)row * a.H + h) * D * ElemT<DT>::bytes + lane * 16;
+    tk = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a.new_k) + src);
+    tv = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a.new_v) + src);
   }
   auto store_token = [&]() {
-    if (write_token) {
-      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(const_cast<void*>(a.k_cache)) + token_dst) = tk;
-      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(const_cast<void*>(a.v_cache)) + token_dst) = tv;
+    if (token_lane && slot >= 0 && slot < a.num_blocks * a.block_size) {
+      const int64_t dst =
+          kv_row_offset(slot / a.block_size, h, slot % a.block_size, a.H, a.block_size, D) * ElemT<DT>::bytes +
+          lane * 16;
+      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(const_cast<void*>(a.k_cache)) + dst) = tk;
+      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(const_cast<void*>(a.v_cache)) + dst) = tv;
     }
   };
   const int ctx = row_ctx(a, row);

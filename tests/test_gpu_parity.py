@@ -872,6 +872,42 @@ def test_mixed_step_graph_replays_match_eager():
         assert torch.isfinite(extra).all()
 
 
+def test_decode_with_cache_write_graph_replays_match_eager():
+    """The decode call with the cache write inside (LLaMA-7B workload)
+    captured as a HIP graph: before every replay the new tokens' slots are
+    overwritten with other values (eager launches); every replay gives the
+    eager output bit for bit and puts the new tokens back into their slots."""
+    wl, _, _ = _config(2)
+    d = wl.decode
+    od = OnDevice(wl)
+    ws = pa.make_decode_workspace(d.num_seqs, wl.num_heads, wl.head_dim, d.max_context_len)
+    out = torch.empty_like(od.q)
+    poison_k = torch.randn_like(od.new_k.float()).to(od.new_k.dtype)
+    poison_v = torch.randn_like(od.new_v.float()).to(od.new_v.dtype)
+
+    def step():
+        pa.paged_attention_decode_with_cache_write(out, od.q, od.k_cache, od.v_cache, od.new_k, od.new_v,
+                                                   od.slot_mapping, od.block_tables, od.context_lens, wl.scale,
+                                                   d.max_context_len, ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref, kref, vref = out.clone(), od.k_cache.clone(), od.v_cache.clone()
+    g = _capture(step)
+    def same(x, y):  # bit for bit (the caches' unused slots hold NaN poison)
+        return torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+    for i in range(4):
+        out.zero_()
+        pa.reshape_and_cache(poison_k, poison_v, od.k_cache, od.v_cache, od.slot_mapping)
+        torch.cuda.synchronize()
+        assert not same(od.k_cache, kref)
+        g.replay()
+        torch.cuda.synchronize()
+        assert same(out, ref), f"output differs on replay {i}"
+        assert same(od.k_cache, kref) and same(od.v_cache, vref), f"caches differ on replay {i}"
+
+
 @pytest.mark.parametrize("side,dtype", [(False, None), (True, None), (True, "f32")])
 def test_attention_step_matches_the_separate_calls(side, dtype):
     """One scheduler iteration in one call (cache write, prefill, decode),
