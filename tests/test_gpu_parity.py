@@ -232,11 +232,12 @@ def test_decode_rows_of_many_partitions():
     _check_attention(od.decode(torch.float32, split=False), ref, "f16")
 
 
-def _fused_rows(wl, pad_rows=()):
+def _fused_rows(wl, pad_rows=(), past_pool_rows=()):
     """Per-row new tokens (fresh values) and slots for the fused decode: a
     row with a context gets its last position's slot, a row in pad_rows and
-    an empty row get slot -1 (nothing written; the row reads the cache as
-    it is)."""
+    an empty row get slot -1, a row in past_pool_rows a slot just past the
+    pool (both skipped: nothing written, the row reads the cache as it
+    is)."""
     from workloads import normal
     d = wl.decode
     S, H, D = d.q.shape
@@ -250,16 +251,18 @@ def _fused_rows(wl, pad_rows=()):
             if r not in pad_rows:
                 slots[r] = wl.new.slot_mapping[t]
             t += 1
+        if r in past_pool_rows:
+            slots[r] = wl.num_blocks * wl.block_size + r
     return nk, nv, slots
 
 
-def _check_fused(wl, split, pad_rows=()):
+def _check_fused(wl, split, pad_rows=(), past_pool_rows=()):
     """pa_paged_attention_decode_with_cache_write against reshape_and_cache
     followed by paged_attention_decode (outputs and caches bit for bit) and
     against the oracle. Both caches first hold the workload's own new tokens
     (so padding rows read finite values); the fresh tokens then replace them."""
     d = wl.decode
-    nk, nv, slots = _fused_rows(wl, pad_rows)
+    nk, nv, slots = _fused_rows(wl, pad_rows, past_pool_rows)
     dt = wl.dtype
     ref = _on_device_written(wl)
     nk_d, nv_d, sl_d = dev(nk, dt), dev(nv, dt), dev(slots)
@@ -289,7 +292,9 @@ def _check_fused(wl, split, pad_rows=()):
         assert np.array_equal(bits(host(st.v_cache)), bits(host(ref.v_cache)))
     kc, vc = oracle.reshape_and_cache(wl.new.k, wl.new.v, wl.k_cache, wl.v_cache, wl.new.slot_mapping,
                                       wl.block_size, dt)
-    kc, vc = oracle.reshape_and_cache(nk, nv, kc, vc, slots, wl.block_size, dt)
+    # the oracle takes in-range slots only: a slot past the pool is the same skip as -1
+    kc, vc = oracle.reshape_and_cache(nk, nv, kc, vc, np.where(slots < wl.num_blocks * wl.block_size, slots, -1),
+                                      wl.block_size, dt)
     _check_attention(out, oracle.decode(d.q, kc, vc, d.block_tables, d.context_lens, wl.scale, dt), dt)
 
 
@@ -311,7 +316,7 @@ def test_decode_with_cache_write_ragged(dtype, D, bs, split):
     ctx = [0, 1, 2, 15, 16, 17, 31, 33, 100, P - 1, P, P + 1, 2 * P + 9, 3 * P, 0, 47]
     wl = decode_workload(f"fused_{dtype}_{D}_{bs}", 640 + bs, dtype, 3, D, bs, ctx,
                          maxb=math.ceil(max(ctx) / bs), pool_factor=1.3)
-    _check_fused(wl, split, pad_rows=(7, 12))
+    _check_fused(wl, split, pad_rows=(7,), past_pool_rows=(12,))
 
 
 def test_decode_empty_context_gives_zeros():
