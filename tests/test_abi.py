@@ -156,6 +156,22 @@ def test_step_args_layout_matches_the_header(tmp_path):
     assert got == want
 
 
+def test_header_is_plain_c(tmp_path):
+    """The boundary is a C ABI: the header compiles as C11 with warnings as
+    errors, and every call it declares can be named from C."""
+    import re
+    import subprocess
+    header = open(os.path.join(ROOT, "include", "pagedattn.h")).read()
+    names = sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\(", header)))
+    src = tmp_path / "uses.c"
+    src.write_text("#include \"pagedattn.h\"\n#include <stdio.h>\nint main(void) {\n"
+                   + "".join(f'  printf("%p\\n", (void*)&{n});\n' for n in names) + "  return 0;\n}\n")
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror",
+                    "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+                    "-c", str(src), "-o", str(tmp_path / "uses.o")], check=True)
+    assert len(names) >= 20
+
+
 def test_attention_step_validation():
     L = pa.lib()
     assert L.pa_attention_step(None, NULL, NULL, NULL, NULL) == pa.PA_ERR_INVALID_ARG
