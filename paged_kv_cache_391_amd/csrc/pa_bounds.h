@@ -50,22 +50,6 @@ __host__ __device__ inline int own_partitions(int ctx, int tok0, int part_tiles)
   return (own_tiles + part_tiles - 1) / part_tiles;
 }
 
-// Tiles [first, first + count) of partition `part` among the `parts` =
-// own_partitions(...) partitions of a row's own_tiles tiles: the tiles are
-// spread evenly, so every partition holds 1 .. part_tiles of them (no short
-// remainder) and the last one ends at own_tiles. A part past the last, or a
-// row without tiles, gets count 0.
-struct PartSpan {
-  int first, count;
-};
-__host__ __device__ inline PartSpan partition_span(int own_tiles, int parts, int part, int part_tiles) {
-  const int per = parts > 0 ? (own_tiles + parts - 1) / parts : part_tiles;
-  const int first = part * per;
-  int count = own_tiles - first;
-  count = count < per ? count : per;
-  return {first, count > 0 ? count : 0};
-}
-
 // Query rows and context of one prefill chunk, from raw query_start_loc
 // entries and context length: rows [q_beg, q_beg + L) with L <= ctx, so the
 // chunk's first query sits at ctx - L >= 0. A range past total_q or a chunk

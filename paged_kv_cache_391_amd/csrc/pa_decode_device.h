@@ -266,13 +266,8 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int b
   // tail of a shared prefix that covers the whole row
   if (part >= (rp.own > 0 ? rp.own : (rp.poff > 0 ? 0 : 1))) return;
 
-  // The row's own tiles spread evenly over its partitions: the count stays
-  // ceil(own tiles / part_tiles) (the workspace slots, the reduction and the
-  // shared-prefix layout depend only on it), but no partition is a short
-  // remainder whose wave would pay a whole start-up for a few tiles.
-  const PartSpan span = partition_span(n_tiles - (rp.tok0 >> 4), rp.own, part, a.part_tiles);
-  const int u0 = (rp.tok0 >> 4) + span.first;
-  const int my_tiles = span.count;
+  const int u0 = (rp.tok0 >> 4) + part * a.part_tiles;
+  const int my_tiles = max(0, min(n_tiles, u0 + a.part_tiles) - u0);
 
   // Fused cache write (decode rows, new_k set): row `row`'s new token sits at
   // position ctx - 1, in the final tile of the row's last partition. That

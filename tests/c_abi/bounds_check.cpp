@@ -51,22 +51,6 @@ int main() {
         CHECK(own_partitions(ctx, 0, single_partition_tiles(M)) <= 1, "ctx %d M %d", ctx, M);
         // split-K on: partition index < the grid's and workspace's count
         CHECK(own_partitions(ctx, 0, P / 16) <= parts, "ctx %d M %d", ctx, M);
-        // the partitions' tile spans: contiguous from the row's first own tile,
-        // 1 .. P/16 tiles each, the last ending at the row's last tile (which
-        // holds a decode step's new token); none past the last
-        for (int tok0 : {0, 16, 512, 1024}) {
-          if (tok0 > ctx) continue;
-          const int own_tiles = tiles_of(ctx) - (tok0 >> 4);
-          const int own = own_partitions(ctx, tok0, P / 16);
-          int next = 0;
-          for (int part = 0; part < own; ++part) {
-            const PartSpan sp = partition_span(own_tiles, own, part, P / 16);
-            CHECK(sp.first == next && sp.count >= 1 && sp.count <= P / 16, "ctx %d tok0 %d part %d", ctx, tok0, part);
-            next = sp.first + sp.count;
-          }
-          CHECK(next == own_tiles, "ctx %d tok0 %d covered %d of %d", ctx, tok0, next, own_tiles);
-          CHECK(partition_span(own_tiles, own, own, P / 16).count == 0, "ctx %d tok0 %d", ctx, tok0);
-        }
         // shared prefix clamped to the row's context (the group minimum is no larger)
         for (int rp : {INT_MIN, -5, 0, 16, 100, 1024, M, M + 16, INT_MAX}) {
           int p = rp < ctx ? rp : ctx;
