@@ -147,28 +147,48 @@ template <Dt DT> __device__ __forceinline__ float dot2one(uint32_t w, uint32_t o
 }
 
 // Work item of this workgroup: sequence s, head h, query tile qt (of QT
-// queries; key tiles of KTP keys price the items). False when the
-// workgroup has none (padding of the grouped grid).
-template <int KTP>
+// queries; key tiles of KTP keys price the items; PER_CU workgroups fit on
+// a compute unit at once). False when the workgroup has none (padding of
+// the grouped grid).
+template <int KTP, int PER_CU>
 __device__ __forceinline__ bool prefill_item(const PrefillArgs& a, int lane, int& s, int& h, int& qt) {
   // Work order. With more workgroups than fit on the chip at once, the
-  // (sequence, head) pairs go in groups of 8: bid = x + 8 (qi + q_tiles grp),
-  // pair = 8 grp + x. Workgroups go round-robin over the 8 XCDs, so all
-  // query tiles of a pair land on one XCD one after another and walk the
-  // same keys together while the K/V tiles sit in that XCD's L2 (each K/V
-  // byte then leaves HBM about once instead of once per query tile).
+  // (sequence, head) pairs go in groups of 8. Workgroups go round-robin over
+  // the 8 XCDs, so workgroup x + 8 i runs on XCD x, and each XCD takes its
+  // workgroups in order as its slots free up.
+  //   * First round (as many whole groups of pairs as the chip holds): bid =
+  //     x + 8 (qi + q_tiles grp) is query tile qi (heaviest first) of pair
+  //     8 grp + x, so all query tiles of a pair run on one XCD together and
+  //     walk the same keys while the K/V tiles sit in that XCD's L2 (each
+  //     K/V byte then leaves HBM about once instead of once per query tile).
+  //   * The rest: each XCD takes the heaviest query tile of each of its
+  //     remaining pairs, then the next heaviest, and so on, so the slots
+  //     that free up first (light first-round tiles) get the heaviest
+  //     second-round tiles and the last to free up the lightest.
   // Otherwise every workgroup is resident at once; the (sequence, query
   // tile) items are then taken heaviest first (priced from the lengths on
   // the device), and the rounds in which the workgroups reach the compute
   // units alternate direction, so heavy and light items share units.
   if (a.grouped) {
-    const int x = blockIdx.x & 7;
-    const int rest = blockIdx.x >> 3;
-    const int pair = (rest / a.q_tiles) * 8 + x;
+    const int pairs_p = (int)gridDim.x / a.q_tiles;  // pairs, padded to a multiple of 8
+    const int p1 = min(pairs_p, a.cus * PER_CU / (8 * a.q_tiles) * 8);  // pairs of the first round
+    const int b = blockIdx.x;
+    int pair, qi;
+    if (b < p1 * a.q_tiles) {
+      const int rest = b >> 3;
+      pair = (rest / a.q_tiles) * 8 + (b & 7);
+      qi = rest % a.q_tiles;
+    } else {  // p1 * q_tiles is a multiple of 8: r keeps bid's XCD
+      const int r = b - p1 * a.q_tiles;
+      const int n2 = (pairs_p - p1) >> 3;  // remaining pairs per XCD
+      const int k = r >> 3;
+      pair = p1 + 8 * (k % n2) + (r & 7);
+      qi = k / n2;
+    }
     if (pair >= a.num_seqs * a.H) return false;
     h = pair % a.H;
     s = pair / a.H;
-    qt = a.q_tiles - 1 - rest % a.q_tiles;
+    qt = a.q_tiles - 1 - qi;
   } else {
     // Workgroups are handed to compute units in order, one per unit per
     // round (workgroup x, x + CUs, x + 2 CUs, ... share a unit). Every
@@ -250,7 +270,7 @@ __global__ __launch_bounds__((PfShape<D, WIDE>::NW * 64))
   const int g4 = lane >> 4;
 
   int h, s, qt;
-  if (!prefill_item<KT>(a, lane, s, h, qt)) return;
+  if (!prefill_item<KT, kPrefillWorkgroupsPerCU>(a, lane, s, h, qt)) return;
   // lengths and row ranges clamped to what the host validated (in-range
   // values are unchanged): no read or write leaves the caller's buffers
   const ChunkRows cr =
@@ -623,7 +643,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void p
   const int g4 = lane >> 4;
 
   int h, s, qt;
-  if (!prefill_item<KTF>(a, lane, s, h, qt)) return;
+  if (!prefill_item<KTF, kPrefillF32WorkgroupsPerCU>(a, lane, s, h, qt)) return;
   const ChunkRows cr =
       chunk_rows(a.query_start_loc[s], a.query_start_loc[s + 1], a.context_lens[s], a.total_q, a.max_context_len);
   const int ctx = cr.ctx, q_beg = cr.q_beg, L = cr.L;
