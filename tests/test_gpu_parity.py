@@ -729,7 +729,9 @@ def test_prefill_many_workgroups_grouped_order(dtype, D, bs):
     """More query tiles than the chip holds at once (15 chunks x 13 heads x 4
     tiles of 128 queries = 780 workgroups, more than 3 per compute unit): the
     kernel then dispatches the query tiles of each (sequence, head) pair
-    together, in groups of 8 pairs (195 pairs leave a partial group). Every
+    together, in groups of 8 pairs, as far as the chip holds them at once,
+    and the pairs after those (a partial group here) by query tile, heaviest
+    first. Every
     output element against the oracle, and the first two chunks bit-identical to a call
     that holds only them (104 workgroups, every one resident at once: the
     plain order, run by the kernel's wide shape of 8 waves x 16 queries
