@@ -34,6 +34,10 @@ MUTANTS = {
         "size_t src = (size_t)pairs[2 * i] * block_bytes, dst = (size_t)pairs[2 * i + 1] * block_bytes;",
         "size_t dst = (size_t)pairs[2 * i] * block_bytes, src = (size_t)pairs[2 * i + 1] * block_bytes;"),
     "copy_of_values_skipped": ("memcpy((char*)v_cache + dst, (const char*)v_cache + src, block_bytes);", ""),
+    "softmax_sum_skips_first_token": ("    sum += x[t];", "    if (t) sum += x[t];"),
+    "scale_applied_twice": ("x[t] = scale * dot;", "x[t] = scale * scale * dot;"),
+    "new_values_written_from_keys": ("memcpy((char*)v_cache + dst, (const char*)v + src, row);",
+                                     "memcpy((char*)v_cache + dst, (const char*)k + src, row);"),
 }
 
 PINS = [
