@@ -65,7 +65,7 @@ MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
 PREFILL_WORKLOADS = ("prefill_long", "prefill_f32")
 KERNEL_SOURCES = ["pa_decode.hip", "pa_decode_device.h", "pa_device.h", "pa_bounds.h", "pa_internal.h"]
 SHARED_KERNEL_SOURCES = KERNEL_SOURCES + ["pa_shared.hip"]
-PREFILL_KERNEL_SOURCES = ["pa_prefill.hip", "pa_device.h", "pa_bounds.h", "pa_internal.h"]
+PREFILL_KERNEL_SOURCES = ["pa_prefill.hip", "pa_grid.h", "pa_device.h", "pa_bounds.h", "pa_internal.h"]
 LEAD_CYCLES = 4_000_000  # GPU spin before each cold step (gpu_lead), ~2 ms
 WARM_LEAD_CYCLES_PER_STEP = 1_000_000  # spin before the back-to-back eager pass, per step queued behind it
 CPU_SECONDS = 10.0  # the oracle repeats its pass until about this much CPU time has elapsed

@@ -45,6 +45,7 @@
 // into a bf16 head and a bf16 remainder (two MFMAs) to keep ~16 bits. A
 // negative scale is applied as |scale| on negated queries (exact: a sign
 // flip), so the max of the raw scores is the max of the scaled ones.
+#include "pa_grid.h"
 #include "pa_internal.h"
 
 #include <type_traits>
@@ -152,39 +153,18 @@ template <Dt DT> __device__ __forceinline__ float dot2one(uint32_t w, uint32_t o
 // the grouped grid).
 template <int KTP, int PER_CU>
 __device__ __forceinline__ bool prefill_item(const PrefillArgs& a, int lane, int& s, int& h, int& qt) {
-  // Work order. With more workgroups than fit on the chip at once, the
-  // (sequence, head) pairs go in groups of 8. Workgroups go round-robin over
-  // the 8 XCDs, so workgroup x + 8 i runs on XCD x, and each XCD takes its
-  // workgroups in order as its slots free up.
-  //   * First round (as many whole groups of pairs as the chip holds): bid =
-  //     x + 8 (qi + q_tiles grp) is query tile qi (heaviest first) of pair
-  //     8 grp + x, so all query tiles of a pair run on one XCD together and
-  //     walk the same keys while the K/V tiles sit in that XCD's L2 (each
-  //     K/V byte then leaves HBM about once instead of once per query tile).
-  //   * The rest: each XCD takes the heaviest query tile of each of its
-  //     remaining pairs, then the next heaviest, and so on, so the slots
-  //     that free up first (light first-round tiles) get the heaviest
-  //     second-round tiles and the last to free up the lightest.
-  // Otherwise every workgroup is resident at once; the (sequence, query
+  // Work order. With more workgroups than fit on the chip at once: the
+  // grouped order of pa_grid.h (every query tile of a pair on one XCD
+  // together in the first round, the heaviest remaining tiles first after
+  // it). Otherwise every workgroup is resident at once; the (sequence, query
   // tile) items are then taken heaviest first (priced from the lengths on
   // the device), and the rounds in which the workgroups reach the compute
   // units alternate direction, so heavy and light items share units.
   if (a.grouped) {
     const int pairs_p = (int)gridDim.x / a.q_tiles;  // pairs, padded to a multiple of 8
-    const int p1 = min(pairs_p, a.cus * PER_CU / (8 * a.q_tiles) * 8);  // pairs of the first round
-    const int b = blockIdx.x;
     int pair, qi;
-    if (b < p1 * a.q_tiles) {
-      const int rest = b >> 3;
-      pair = (rest / a.q_tiles) * 8 + (b & 7);
-      qi = rest % a.q_tiles;
-    } else {  // p1 * q_tiles is a multiple of 8: r keeps bid's XCD
-      const int r = b - p1 * a.q_tiles;
-      const int n2 = (pairs_p - p1) >> 3;  // remaining pairs per XCD
-      const int k = r >> 3;
-      pair = p1 + 8 * (k % n2) + (r & 7);
-      qi = k / n2;
-    }
+    grouped_item(blockIdx.x, a.q_tiles, pairs_p, grouped_first_round_pairs(a.cus * PER_CU, a.q_tiles, pairs_p), pair,
+                 qi);
     if (pair >= a.num_seqs * a.H) return false;
     h = pair % a.H;
     s = pair / a.H;

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <vector>
 
+#include "../../paged_kv_cache_391_amd/csrc/pa_grid.h"
 #include "../../paged_kv_cache_391_amd/csrc/pa_internal.h"
 
 using namespace pa;
@@ -84,6 +85,30 @@ int main() {
       const int32_t c = clamp_block(b, nb);
       CHECK(c >= 0 && c < nb, "id %d nb %d -> %d", b, nb, c);
       if (b >= 0 && b < nb) CHECK(c == b, "in-range id %d changed to %d", b, c);
+    }
+  }
+  // the prefill's grouped work order (pa_grid.h): every workgroup of a grid
+  // of q_tiles * pairs_p maps to a distinct (pair, query tile), all of them
+  // are covered, and each workgroup runs on its pair's XCD (pair mod 8)
+  for (int q_tiles : {1, 2, 3, 4, 5, 7, 16, 33, 128}) {
+    for (int pairs_p : {8, 16, 24, 200, 320, 1000, 4096}) {
+      for (int slots : {0, 1, 8, 24, 96, 512, 768, 912, 3000, 1 << 20}) {
+        ++cases;
+        const int p1 = grouped_first_round_pairs(slots, q_tiles, pairs_p);
+        CHECK(p1 % 8 == 0 && p1 >= 0 && p1 <= pairs_p && (int64_t)p1 * q_tiles <= slots,
+              "first round: %d pairs of %d tiles for %d slots", p1, q_tiles, slots);
+        std::vector<char> seen((size_t)pairs_p * q_tiles, 0);
+        bool ok = true;
+        for (int b = 0; b < q_tiles * pairs_p && ok; ++b) {
+          int pair = -1, qi = -1;
+          grouped_item(b, q_tiles, pairs_p, p1, pair, qi);
+          ok = pair >= 0 && pair < pairs_p && qi >= 0 && qi < q_tiles && !seen[(size_t)pair * q_tiles + qi] &&
+               (pair & 7) == (b & 7);
+          if (ok) seen[(size_t)pair * q_tiles + qi] = 1;
+          CHECK(ok, "q_tiles %d pairs %d slots %d: workgroup %d -> pair %d tile %d", q_tiles, pairs_p, slots, b, pair,
+                qi);
+        }
+      }
     }
   }
   if (fails) {
