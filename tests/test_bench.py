@@ -149,3 +149,25 @@ def test_bench_prefill_long_prints_the_mfma_roofline():
     rf = rec["roofline"]
     assert rf["bound"] == "mfma" and rf["unit"] == "TFLOP/s" and rf["peak"] == 2500.0
     assert 0.05 < rf["frac"] < 1.0 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
+
+
+def _local_includes(name, seen=None):
+    """The csrc files a source pulls in through quoted includes, itself included."""
+    import re
+    seen = set() if seen is None else seen
+    if name in seen:
+        return seen
+    seen.add(name)
+    text = open(os.path.join(ROOT, "paged_kv_cache_391_amd", "csrc", name)).read()
+    for inc in re.findall(r'^#include "([^"/]+)"', text, flags=re.M):
+        _local_includes(inc, seen)
+    return seen
+
+
+def test_traffic_hashes_cover_every_file_the_kernels_are_built_from():
+    """A traffic record stays in use only while the hash of the listed kernel
+    sources matches; a header the kernel includes but the list misses could
+    change the kernel without retiring the record."""
+    assert _local_includes("pa_decode.hip") <= set(bench.KERNEL_SOURCES)
+    assert _local_includes("pa_shared.hip") <= set(bench.SHARED_KERNEL_SOURCES)
+    assert _local_includes("pa_prefill.hip") <= set(bench.PREFILL_KERNEL_SOURCES)
